@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Throughput of the routed-attention hot path on one MI355X.
+
+Metric: routed-attention prefill tok/s at 32K and decode tok/s at 32K context,
+with the fraction of the bf16 MFMA peak (prefill) and of the HBM peak (decode).
+
+Prefill step (the JSON line's `value`), Qwen3-4B-shaped, 32768 tokens, 32 q /
+8 kv heads, head_dim 128, bf16 N(0,1) inputs resident in HBM:
+  flux_route      hidden [32768][2560] bf16 -> MLP 2560 -> 256 -> 2 -> route;
+                  the seeded N(0, 0.02) weights carry output biases (+1, -1)
+                  so layer 0 routes to FA and layer 1 to SA: the workload runs
+                  FA and SA on identical inputs, and the kernels read the
+                  router's output on the device (no host sync);
+  flux_build_block_mask  SA mask, blocks of 128, 1 sink block, window 2048;
+  flux_attn_prefill x 2  layer 0 (FA) and layer 1 (SA) on the same q/k/v.
+  value = 32768 tokens / step time.
+Decode phase (the "decode" object): 16 sequences x 32768 cached tokens, 36
+layers with distinct caches (72 GiB), a seeded route with exactly 18 SA layers;
+one step = 36 flux_attn_decode calls; tok/s = 16 / step time.
+
+Roofline: the dominant kernel is the prefill kernel; achieved = algorithmic
+(computed-block) flops of its launches / their summed duration, timed with HIP
+events on the launch stream.  Computed-block flops per layer =
+active 128x128 blocks * 4 * 128^2 * head_dim * hq (FA: all 32896 causal
+blocks; SA: 4216 blocks).  Decode bytes per step = K+V bytes the layers must
+read (FA: all 32768 keys, SA: 17 blocks of 128 keys).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "routed-attention prefill tok/s @32K & decode tok/s @32K ctx; % MFMA / HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=10)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 256 MiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path would shard by KV-head group or by sequence, see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    lib = os.path.join(ROOT, "block_sparse_attention_flux_amd", "lib", "libflux.so")
+    if not os.path.exists(lib):
+        import __graft_entry__
+        __graft_entry__.build()
+    import block_sparse_attention_flux_amd as flux
+    from synth import inputs as syn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ------------------------------------------------------------ prefill inputs
+    wl = syn.PREFILL32K
+    S, hq, hkv, d = wl.seqlens[0], wl.hq, wl.hkv, wl.head_dim
+    sa = flux.SAParams(wl.block_size, wl.sink_blocks, wl.local_blocks)
+    g = syn.generator(wl.seed, dev)
+    hidden = syn.normal((S, wl.hidden_dim), g, dev)
+    q = syn.normal((S, hq, d), g, dev)
+    k = syn.normal((S, hkv, d), g, dev)
+    v = syn.normal((S, hkv, d), g, dev)
+    w1, b1, w2, b2 = syn.router_weights(wl.hidden_dim, wl.router_h1, wl.n_layers, wl.seed)
+    b2 = b2 + torch.tensor([1.0, -1.0])  # layer 0 -> FA, layer 1 -> SA
+    w1, b1, w2, b2 = (t.to(dev) for t in (w1, b1, w2, b2))
+    cu = syn.cu_seqlens([S], dev)
+    nb = flux.mask_blocks(S, sa)
+    nnz = flux.mask_nnz(S, sa)
+    route = torch.empty((1, wl.n_layers), dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
+    out = [torch.empty_like(q) for _ in range(wl.n_layers)]
+    L = flux._lib
+    F = flux._LIB
+    cstream = __import__("ctypes").c_void_p(stream.cuda_stream)
+
+    def P(t):
+        return __import__("ctypes").c_void_p(t.data_ptr())
+
+    def check(code, what):
+        if code != 0:
+            raise RuntimeError(f"{what} failed: {flux.status_str(code)}")
+
+    def route_call():
+        check(F.flux_route(P(hidden), L.FLUX_BF16, P(cu), 1, wl.hidden_dim, P(w1), P(b1), wl.router_h1,
+                           P(w2), P(b2), wl.n_layers, P(route), None, cstream), "flux_route")
+
+    def mask_call():
+        check(F.flux_build_block_mask(S, sa.c(), None, P(row_ptr), P(col_idx), cstream), "mask")
+
+    def prefill_call(layer):
+        check(F.flux_attn_prefill(P(q), P(k), P(v), P(out[layer]), P(cu), 1, S, hq, hkv, d,
+                                  1.0 / math.sqrt(d), P(route), wl.n_layers, layer, P(row_ptr),
+                                  P(col_idx), nb, sa.c(), cstream), "prefill")
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def prefill_step(timers=None):
+        if timers is None:
+            route_call(); mask_call(); prefill_call(0); prefill_call(1)
+            return
+        e = [ev() for _ in range(5)]
+        e[0].record(stream); route_call(); mask_call()
+        e[1].record(stream); prefill_call(0)
+        e[2].record(stream); prefill_call(1)
+        e[3].record(stream)
+        timers.append(e)
+
+    log(f"prefill warmup x{args.warmup}")
+    for _ in range(args.warmup):
+        prefill_step()
+    torch.cuda.synchronize()
+    assert route[0].tolist() == [1, 0], f"router did not produce the FA/SA split: {route.tolist()}"
+
+    log(f"prefill timed x{args.steps}")
+    timers = []
+    t0, t1 = ev(), ev()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        prefill_step(timers)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / args.steps
+    rm = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                   for e in timers])
+    router_mask_ms, fa_ms, sa_ms = (float(x) for x in rm.mean(axis=0))
+    blk_flops = 4.0 * wl.block_size ** 2 * d * hq
+    fa_flops = nb * (nb + 1) / 2 * blk_flops
+    sa_flops = nnz * blk_flops
+    pre_tflops = (fa_flops + sa_flops) / ((fa_ms + sa_ms) * 1e-3) / 1e12
+    value = S / (step_ms * 1e-3)
+    log(f"prefill step {step_ms:.3f} ms  FA {fa_ms:.3f} ms ({fa_flops / fa_ms / 1e9:.1f} TF/s)  "
+        f"SA {sa_ms:.3f} ms ({sa_flops / sa_ms / 1e9:.1f} TF/s)  router+mask {router_mask_ms:.3f} ms")
+
+    if args.copy_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: 268435456 bytes read, 268435456 bytes written")
+        del src, dst
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 q/k/v and hidden states, seeded N(0,0.02) router",
+        "config": {
+            "workload": "Qwen3-4B-shaped routed prefill, 32768 tokens, 1 FA + 1 SA layer on identical inputs",
+            "global_batch": 1, "seq_len": S, "hq": hq, "hkv": hkv, "head_dim": d,
+            "sa": {"block": wl.block_size, "sink_blocks": wl.sink_blocks, "local_blocks": wl.local_blocks},
+            "router": f"{wl.hidden_dim}->{wl.router_h1}->{wl.n_layers}", "parallelism": "single GPU",
+        },
+        "prefill": {
+            "fa_ms": round(fa_ms, 4), "sa_ms": round(sa_ms, 4), "router_mask_ms": round(router_mask_ms, 4),
+            "fa_tflops": round(fa_flops / fa_ms / 1e9, 1), "sa_tflops": round(sa_flops / sa_ms / 1e9, 1),
+            "fa_frac_mfma": round(fa_flops / fa_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "sa_frac_mfma": round(sa_flops / sa_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "fa_tok_s": round(S / (fa_ms * 1e-3), 1), "sa_tok_s": round(S / (sa_ms * 1e-3), 1),
+        },
+        "roofline": {
+            "kernel": "prefill_kernel<128,128> (FA + SA launches)",
+            "bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    del hidden
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ decode phase
+    if not args.no_decode:
+        result["decode"] = run_decode(args, flux, syn, dev, stream, log)
+
+    # ------------------------------------------------------------ oracle on the host
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, q, k, v, S, wl, log)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def run_decode(args, flux, syn, dev, stream, log):
+    import numpy as np
+    import torch
+
+    wl = syn.DECODE32K
+    n_seq, ctx = len(wl.seqlens), wl.seqlens[0]
+    hq, hkv, d, nl = wl.hq, wl.hkv, wl.head_dim, wl.n_layers
+    sa = flux.SAParams(wl.block_size, wl.sink_blocks, wl.local_blocks)
+    g = syn.generator(wl.seed, dev)
+    log(f"decode: allocating {nl} layers x 2 x {n_seq * hkv * ctx * d * 2 / 2**30:.1f} GiB caches")
+    kc = [syn.normal((n_seq, hkv, ctx, d), g, dev) for _ in range(nl)]
+    vc = [syn.normal((n_seq, hkv, ctx, d), g, dev) for _ in range(nl)]
+    q = [syn.normal((n_seq, hq, d), g, dev) for _ in range(nl)]
+    out = torch.empty((n_seq, hq, d), dtype=torch.bfloat16, device=dev)
+    route_vec = syn.seeded_route(nl, wl.n_sa_layers, wl.seed)
+    route = route_vec[None].repeat(n_seq, 1).to(dev).contiguous()
+    seqlens = torch.full((n_seq,), ctx, dtype=torch.int32, device=dev)
+    _, rp, ci = flux.build_block_mask(ctx, sa, device=dev, dense=False)
+    ws = torch.empty(flux.decode_workspace_size(n_seq, hq, hkv, d, ctx), dtype=torch.uint8, device=dev)
+
+    def step(timers=None):
+        for layer in range(nl):
+            if timers is not None:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                timers.append(e)
+            flux.attn_decode(q[layer], kc[layer], vc[layer], seqlens, route, layer, rp, ci, sa, ws, out)
+        if timers is not None:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            timers.append(e)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"decode timed x{args.decode_steps}")
+    per_step = []
+    lay = np.zeros(nl)
+    for _ in range(args.decode_steps):
+        tm = []
+        step(tm)
+        torch.cuda.synchronize()
+        per_step.append(tm[0].elapsed_time(tm[-1]))
+        lay += np.array([tm[i].elapsed_time(tm[i + 1]) for i in range(nl)])
+    lay /= args.decode_steps
+    step_ms = float(np.mean(per_step))
+    fa_layers = [i for i in range(nl) if int(route_vec[i]) == 1]
+    sa_layers = [i for i in range(nl) if int(route_vec[i]) == 0]
+    sa_keys = (wl.sink_blocks + wl.local_blocks) * wl.block_size
+    kv_bytes_tok = hkv * d * 2 * 2 * n_seq
+    fa_bytes = ctx * kv_bytes_tok
+    sa_bytes = sa_keys * kv_bytes_tok
+    step_bytes = len(fa_layers) * fa_bytes + len(sa_layers) * sa_bytes
+    fa_ms = float(lay[fa_layers].mean())
+    sa_ms = float(lay[sa_layers].mean())
+    gbs = step_bytes / (step_ms * 1e-3) / 1e9
+    fa_gbs = fa_bytes / (fa_ms * 1e-3) / 1e9
+    log(f"decode step {step_ms:.3f} ms ({16 / step_ms * 1e3:.0f} tok/s)  FA layer {fa_ms:.3f} ms "
+        f"({fa_gbs:.0f} GB/s)  SA layer {sa_ms:.3f} ms ({sa_bytes / sa_ms / 1e6:.0f} GB/s)")
+    res = {
+        "workload": "Qwen3-4B-shaped decode, 16 seqs x 32768 ctx, 36 layers (18 FA / 18 SA seeded)",
+        "value": round(n_seq / (step_ms * 1e-3), 1), "unit": "tok/s",
+        "ms_per_step": round(step_ms, 4), "steps": args.decode_steps,
+        "fa_layer_ms": round(fa_ms, 4), "sa_layer_ms": round(sa_ms, 4),
+        "bytes_per_step": step_bytes,
+        "roofline": {"kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",
+                     "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "fa_layer_gbs": round(fa_gbs, 1),
+                     "sa_layer_gbs": round(sa_bytes / sa_ms / 1e6, 1)},
+    }
+    del kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(args, q, k, v, S, wl, log):
+    """The float64 oracle, as it stands, on a bounded sample of the same
+    prefill workload: router + mask in full, then FA and SA layer rows sampled
+    uniformly over the prompt (all heads) until the time budget is spent."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    log(f"cpu baseline: oracle on host ({cores} cores visible, BLAS threads {threads})")
+    qf = q.float().cpu().numpy()
+    kf = k.float().cpu().numpy()
+    vf = v.float().cpu().numpy()
+    rng = np.random.default_rng(0)
+    t_start = time.perf_counter()
+    nb = oracle.num_blocks(S, wl.block_size)
+    m = oracle.block_mask(nb, wl.sink_blocks, wl.local_blocks)
+    t_mask = time.perf_counter() - t_start
+    rows_done = 0
+    t_rows = 0.0
+    while t_rows < args.cpu_seconds:
+        rows = np.sort(rng.integers(0, S, size=8))
+        t0 = time.perf_counter()
+        oracle.attention_prefill(qf, kf, vf, True, m, wl.block_size, rows=rows)
+        oracle.attention_prefill(qf, kf, vf, False, m, wl.block_size, rows=rows)
+        t_rows += time.perf_counter() - t0
+        rows_done += len(rows)
+    per_row = t_rows / rows_done
+    tok_s = 1.0 / per_row  # mask/router are per prompt: amortised below
+    full_prompt_s = per_row * S + t_mask
+    log(f"cpu baseline: {rows_done} rows in {t_rows:.1f} s -> {S / full_prompt_s:.2f} tok/s")
+    return {"value": round(S / full_prompt_s, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done} query rows sampled uniformly from the 32768-token prompt, all 32 heads, "
+                      f"FA + SA layer each ({t_rows:.1f} s), plus the mask build; scaled to a full prompt",
+            "per_row_ms": round(per_row * 1e3, 3), "rows_per_s": round(tok_s, 2)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

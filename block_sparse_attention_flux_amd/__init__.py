@@ -1,0 +1,179 @@
+"""Layer-routed hybrid attention (Flux Attention) for MI355X / gfx950.
+
+Thin Python binding over libflux.so: every function below only checks and
+marshals arguments (torch tensors -> device pointers, the current HIP stream)
+and calls the C entry point of the same name in include/flux.h.  All the
+computation runs in the library's HIP kernels; there is no fallback path, and
+importing this package fails if the library has not been built.
+
+    route, logits = route(hidden, cu_seqlens, w1, b1, w2, b2)
+    mask, row_ptr, col_idx = build_block_mask(max_seqlen, sa)
+    out = attn_prefill(q, k, v, cu_seqlens, max_seqlen, route, layer, row_ptr, col_idx, sa)
+    out = attn_decode(q, k_cache, v_cache, seqlens, route, layer, row_ptr, col_idx, sa, ws)
+"""
+
+import ctypes
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+_LIB = _lib.load()
+
+__all__ = [
+    "SAParams", "FluxError", "route", "mask_blocks", "mask_nnz", "build_block_mask",
+    "attn_prefill", "decode_workspace_size", "attn_decode", "status_str",
+]
+
+
+@dataclass(frozen=True)
+class SAParams:
+    """Sparse Attention block pattern: ``sink_blocks`` sink blocks plus a
+    causal window of ``local_blocks`` blocks (diagonal included), blocks of
+    ``block_size`` tokens."""
+    block_size: int = 128
+    sink_blocks: int = 1
+    local_blocks: int = 16
+
+    def c(self):
+        return _lib.SAParamsC(self.block_size, self.sink_blocks, self.local_blocks)
+
+
+class FluxError(RuntimeError):
+    """The HIP runtime reported an error inside libflux."""
+
+
+def status_str(code):
+    return _LIB.flux_status_str(int(code)).decode()
+
+
+def _check(code, what):
+    if code == _lib.FLUX_OK:
+        return
+    msg = f"{what}: {status_str(code)} (status {code})"
+    if code == _lib.FLUX_ERR_HIP:
+        raise FluxError(msg)
+    raise ValueError(msg)
+
+
+def _ptr(t, dtype=None, name="tensor", device=True):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def route(hidden, cu_seqlens, w1, b1, w2, b2, route_out=None, logits_out=None):
+    """Layer Router (flux_route): returns (route uint8 [n_req][L], logits fp32 or None)."""
+    if hidden.dtype == torch.bfloat16:
+        dt = _lib.FLUX_BF16
+    elif hidden.dtype == torch.float32:
+        dt = _lib.FLUX_F32
+    else:
+        raise ValueError("hidden must be bfloat16 or float32")
+    n_req = cu_seqlens.numel() - 1
+    h1, d_in = w1.shape
+    n_layers = w2.shape[0]
+    if route_out is None:
+        route_out = torch.empty((n_req, n_layers), dtype=torch.uint8, device=hidden.device)
+    code = _LIB.flux_route(
+        _ptr(hidden, None, "hidden"), dt, _ptr(cu_seqlens, torch.int32, "cu_seqlens"), n_req, d_in,
+        _ptr(w1, torch.float32, "w1"), _ptr(b1, torch.float32, "b1"), h1,
+        _ptr(w2, torch.float32, "w2"), _ptr(b2, torch.float32, "b2"), n_layers,
+        _ptr(route_out, torch.uint8, "route_out"), _ptr(logits_out, torch.float32, "logits_out"),
+        _stream(hidden.device))
+    _check(code, "flux_route")
+    return route_out, logits_out
+
+
+def mask_blocks(seqlen, sa):
+    n = _LIB.flux_mask_blocks(int(seqlen), sa.c())
+    if n < 0:
+        _check(int(n), "flux_mask_blocks")
+    return int(n)
+
+
+def mask_nnz(seqlen, sa):
+    n = _LIB.flux_mask_nnz(int(seqlen), sa.c())
+    if n < 0:
+        _check(int(n), "flux_mask_nnz")
+    return int(n)
+
+
+def build_block_mask(seqlen, sa, device="cuda", dense=True):
+    """SA block mask (flux_build_block_mask): (mask uint8 [nb][nb] or None,
+    row_ptr int32 [nb+1], col_idx int32 [nnz])."""
+    nb = mask_blocks(seqlen, sa)
+    nnz = mask_nnz(seqlen, sa)
+    mask = torch.empty((nb, nb), dtype=torch.uint8, device=device) if dense else None
+    row_ptr = torch.empty(nb + 1, dtype=torch.int32, device=device)
+    col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
+    code = _LIB.flux_build_block_mask(int(seqlen), sa.c(), _ptr(mask, torch.uint8, "mask"),
+                                      _ptr(row_ptr), _ptr(col_idx), _stream(row_ptr.device))
+    _check(code, "flux_build_block_mask")
+    return mask, row_ptr, col_idx[:nnz]
+
+
+def attn_prefill(q, k, v, cu_seqlens, max_seqlen, route, layer, row_ptr, col_idx, sa,
+                 out=None, softmax_scale=None):
+    """One routed attention layer over packed prompts (flux_attn_prefill)."""
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (T, hkv, d) or v.shape != (T, hkv, d):
+        raise ValueError("k and v must be [T][hkv][head_dim] like q")
+    if out is None:
+        out = torch.empty_like(q)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    code = _LIB.flux_attn_prefill(
+        _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"),
+        _ptr(out, torch.bfloat16, "out"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
+        cu_seqlens.numel() - 1, int(max_seqlen), hq, hkv, d, float(softmax_scale),
+        _ptr(route, torch.uint8, "route"), route.shape[-1], int(layer),
+        _ptr(row_ptr, torch.int32, "row_ptr"), _ptr(col_idx, torch.int32, "col_idx"),
+        row_ptr.numel() - 1, sa.c(), _stream(q.device))
+    _check(code, "flux_attn_prefill")
+    return out
+
+
+def decode_workspace_size(n_seq, hq, hkv, head_dim, max_len):
+    return int(_LIB.flux_attn_decode_workspace_size(n_seq, hq, hkv, head_dim, max_len))
+
+
+def attn_decode(q, k_cache, v_cache, seqlens, route, layer, row_ptr, col_idx, sa,
+                workspace=None, out=None, softmax_scale=None):
+    """One split-KV decode step of one layer (flux_attn_decode)."""
+    n_seq, hq, d = q.shape
+    _, hkv, max_len, _ = k_cache.shape
+    if k_cache.shape != (n_seq, hkv, max_len, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [n_seq][hkv][max_len][head_dim]")
+    if out is None:
+        out = torch.empty_like(q)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        ws_bytes = decode_workspace_size(n_seq, hq, hkv, d, max_len)
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    code = _LIB.flux_attn_decode(
+        _ptr(q, torch.bfloat16, "q"), _ptr(k_cache, torch.bfloat16, "k_cache"),
+        _ptr(v_cache, torch.bfloat16, "v_cache"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(seqlens, torch.int32, "seqlens"), n_seq, max_len, hq, hkv, d, float(softmax_scale),
+        _ptr(route, torch.uint8, "route"), route.shape[-1], int(layer),
+        _ptr(row_ptr, torch.int32, "row_ptr"), _ptr(col_idx, torch.int32, "col_idx"),
+        row_ptr.numel() - 1, sa.c(), _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(code, "flux_attn_decode")
+    return out

@@ -1,0 +1,169 @@
+// extern "C" entry points of libflux: host-side validation, then dispatch to
+// the kernels.  Declared and documented in include/flux.h.
+#include "flux.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "flux_internal.h"
+
+namespace {
+
+bool sa_params_ok(const flux_sa_params& p) {
+  return p.sink_blocks >= 0 && p.local_blocks >= 1;
+}
+bool block_supported(int32_t b) { return b == 64 || b == 128; }
+bool head_dim_supported(int32_t d) { return d == 64 || d == 128; }
+
+int64_t window_prefix(int64_t n, int64_t w) {
+  return n <= w ? n * (n + 1) / 2 : w * (w + 1) / 2 + (n - w) * w;
+}
+int64_t sink_prefix(int64_t n, int64_t s, int64_t w) {
+  const int64_t t = n - w;
+  if (t <= 0 || s <= 0) return 0;
+  return t <= s ? t * (t + 1) / 2 : s * (s + 1) / 2 + (t - s) * s;
+}
+
+flux_status from_hip(hipError_t e) { return e == hipSuccess ? FLUX_OK : FLUX_ERR_HIP; }
+
+// Checks shared by prefill and decode.
+flux_status check_attn_common(int32_t hq, int32_t hkv, int32_t head_dim, float scale,
+                              const uint8_t* route, int32_t n_layers, int32_t layer,
+                              const int32_t* row_ptr, const int32_t* col_idx,
+                              int32_t mask_blocks, int32_t covered_len, flux_sa_params p) {
+  if (route == nullptr || row_ptr == nullptr || col_idx == nullptr) return FLUX_ERR_INVALID_ARG;
+  if (hq < 1 || hkv < 1 || hq % hkv != 0) return FLUX_ERR_INVALID_ARG;
+  if (n_layers < 1 || layer < 0 || layer >= n_layers) return FLUX_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || scale > 1e30f) return FLUX_ERR_INVALID_ARG;
+  if (!sa_params_ok(p)) return FLUX_ERR_INVALID_ARG;
+  if (!head_dim_supported(head_dim) || !block_supported(p.block_size)) return FLUX_ERR_UNSUPPORTED;
+  if (hq / hkv > 16) return FLUX_ERR_UNSUPPORTED;
+  const int64_t need = (static_cast<int64_t>(covered_len) + p.block_size - 1) / p.block_size;
+  if (mask_blocks < need) return FLUX_ERR_INVALID_ARG;
+  return FLUX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flux_status_str(int32_t status) {
+  switch (status) {
+    case FLUX_OK: return "ok";
+    case FLUX_ERR_INVALID_ARG: return "invalid argument";
+    case FLUX_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FLUX_ERR_WORKSPACE: return "workspace missing or too small";
+    case FLUX_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+flux_status flux_route(const void* hidden, int32_t hidden_dtype, const int32_t* cu_seqlens,
+                       int32_t n_req, int32_t d_in, const float* w1, const float* b1, int32_t h1,
+                       const float* w2, const float* b2, int32_t n_layers, uint8_t* route_out,
+                       float* logits_out, void* stream) {
+  if (hidden == nullptr || cu_seqlens == nullptr || w1 == nullptr || b1 == nullptr ||
+      w2 == nullptr || b2 == nullptr || route_out == nullptr)
+    return FLUX_ERR_INVALID_ARG;
+  if (hidden_dtype != FLUX_F32 && hidden_dtype != FLUX_BF16) return FLUX_ERR_INVALID_ARG;
+  if (n_req < 1 || d_in < 1 || h1 < 1 || n_layers < 1) return FLUX_ERR_INVALID_ARG;
+  if (d_in > 8192 || h1 > 4096 || n_layers > 4096) return FLUX_ERR_UNSUPPORTED;
+  if (n_req > INT32_MAX / 2) return FLUX_ERR_INVALID_ARG;
+  return from_hip(flux::launch_route(hidden, hidden_dtype == FLUX_BF16, cu_seqlens, n_req, d_in,
+                                     w1, b1, h1, w2, b2, n_layers, route_out, logits_out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int64_t flux_mask_blocks(int32_t seqlen, flux_sa_params p) {
+  if (seqlen < 1 || p.block_size < 1) return FLUX_ERR_INVALID_ARG;
+  return (static_cast<int64_t>(seqlen) + p.block_size - 1) / p.block_size;
+}
+
+int64_t flux_mask_nnz(int32_t seqlen, flux_sa_params p) {
+  if (seqlen < 1 || p.block_size < 1 || !sa_params_ok(p)) return FLUX_ERR_INVALID_ARG;
+  const int64_t nb = (static_cast<int64_t>(seqlen) + p.block_size - 1) / p.block_size;
+  return window_prefix(nb, p.local_blocks) + sink_prefix(nb, p.sink_blocks, p.local_blocks);
+}
+
+flux_status flux_build_block_mask(int32_t seqlen, flux_sa_params p, uint8_t* mask_out,
+                                  int32_t* row_ptr, int32_t* col_idx, void* stream) {
+  if (row_ptr == nullptr || col_idx == nullptr) return FLUX_ERR_INVALID_ARG;
+  if (seqlen < 1 || !sa_params_ok(p)) return FLUX_ERR_INVALID_ARG;
+  if (!block_supported(p.block_size)) return FLUX_ERR_UNSUPPORTED;
+  const int64_t nb = flux_mask_blocks(seqlen, p);
+  if (nb > 65536) return FLUX_ERR_UNSUPPORTED;
+  if (flux_mask_nnz(seqlen, p) > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
+  return from_hip(flux::launch_build_mask(static_cast<int32_t>(nb), p.sink_blocks, p.local_blocks,
+                                          mask_out, row_ptr, col_idx,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+flux_status flux_attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              uint16_t* out, const int32_t* cu_seqlens, int32_t n_req,
+                              int32_t max_seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
+                              float softmax_scale, const uint8_t* route, int32_t n_layers,
+                              int32_t layer, const int32_t* mask_row_ptr,
+                              const int32_t* mask_col_idx, int32_t mask_blocks, flux_sa_params p,
+                              void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || cu_seqlens == nullptr)
+    return FLUX_ERR_INVALID_ARG;
+  if (out == q || out == k || out == v) return FLUX_ERR_INVALID_ARG;
+  if (n_req < 1 || max_seqlen < 1) return FLUX_ERR_INVALID_ARG;
+  const flux_status st = check_attn_common(hq, hkv, head_dim, softmax_scale, route, n_layers, layer,
+                                           mask_row_ptr, mask_col_idx, mask_blocks, max_seqlen, p);
+  if (st != FLUX_OK) return st;
+  const int64_t n_qt = (static_cast<int64_t>(max_seqlen) + p.block_size - 1) / p.block_size;
+  if (n_qt * hq * n_req > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
+  flux::PrefillParams pp{};
+  pp.q = q; pp.k = k; pp.v = v; pp.out = out;
+  pp.cu_seqlens = cu_seqlens; pp.route = route;
+  pp.row_ptr = mask_row_ptr; pp.col_idx = mask_col_idx;
+  pp.n_req = n_req; pp.max_seqlen = max_seqlen; pp.hq = hq; pp.hkv = hkv;
+  pp.head_dim = head_dim; pp.n_layers = n_layers; pp.layer = layer;
+  pp.mask_blocks = mask_blocks; pp.block_size = p.block_size;
+  pp.sink_blocks = p.sink_blocks; pp.local_blocks = p.local_blocks;
+  pp.scale = softmax_scale;
+  return from_hip(flux::launch_prefill(pp, static_cast<hipStream_t>(stream)));
+}
+
+size_t flux_attn_decode_workspace_size(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_dim,
+                                       int32_t max_len) {
+  if (n_seq < 1 || hq < 1 || hkv < 1 || head_dim < 1 || max_len < 1) return 0;
+  const size_t ns = static_cast<size_t>(flux::decode_splits(n_seq, hkv, max_len));
+  const size_t slots = static_cast<size_t>(n_seq) * hq * ns;
+  return slots * (static_cast<size_t>(head_dim) + 2) * sizeof(float);
+}
+
+flux_status flux_attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                             uint16_t* out, const int32_t* seqlens, int32_t n_seq,
+                             int32_t max_len, int32_t hq, int32_t hkv, int32_t head_dim,
+                             float softmax_scale, const uint8_t* route, int32_t n_layers,
+                             int32_t layer, const int32_t* mask_row_ptr,
+                             const int32_t* mask_col_idx, int32_t mask_blocks, flux_sa_params p,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr ||
+      seqlens == nullptr)
+    return FLUX_ERR_INVALID_ARG;
+  if (out == q) return FLUX_ERR_INVALID_ARG;
+  if (n_seq < 1 || max_len < 1) return FLUX_ERR_INVALID_ARG;
+  const flux_status st = check_attn_common(hq, hkv, head_dim, softmax_scale, route, n_layers, layer,
+                                           mask_row_ptr, mask_col_idx, mask_blocks, max_len, p);
+  if (st != FLUX_OK) return st;
+  const int32_t ns = flux::decode_splits(n_seq, hkv, max_len);
+  if (static_cast<int64_t>(n_seq) * hkv * ns > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
+  const size_t need = flux_attn_decode_workspace_size(n_seq, hq, hkv, head_dim, max_len);
+  if (ns > 1 && (workspace == nullptr || workspace_bytes < need)) return FLUX_ERR_WORKSPACE;
+  flux::DecodeParams dp{};
+  dp.q = q; dp.k_cache = k_cache; dp.v_cache = v_cache; dp.out = out;
+  dp.seqlens = seqlens; dp.route = route; dp.row_ptr = mask_row_ptr; dp.col_idx = mask_col_idx;
+  const size_t slots = static_cast<size_t>(n_seq) * hq * ns;
+  dp.part_o = static_cast<float*>(workspace);
+  dp.part_ml = workspace != nullptr ? static_cast<float*>(workspace) + slots * head_dim : nullptr;
+  dp.n_seq = n_seq; dp.max_len = max_len; dp.hq = hq; dp.hkv = hkv; dp.head_dim = head_dim;
+  dp.n_layers = n_layers; dp.layer = layer; dp.mask_blocks = mask_blocks;
+  dp.block_size = p.block_size; dp.nsplit = ns; dp.scale = softmax_scale;
+  return from_hip(flux::launch_decode(dp, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

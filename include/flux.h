@@ -1,0 +1,181 @@
+/*
+ * flux.h -- C ABI of the MI355X (gfx950) layer-routed hybrid attention library
+ * (libflux.so).
+ *
+ * The method: Flux Attention adds a light Layer Router to a frozen LLM.  The
+ * router pools the first and the last 100 prompt tokens, runs an MLP and
+ * thresholds its output to a hard per-layer choice between Full Attention (FA)
+ * and block-Sparse Attention (SA); the route is decided once at prefill and
+ * reused by every decode step, and SA layers read only a minimal KV set.
+ * (Flux Attention abstract, arXiv 2604.07394; technical summary on
+ * gist.science, section 2 "Methodology".)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked [device] are HIP device pointers; [host] are host memory.
+ *   The caller allocates and frees every buffer.  The library keeps no mutable
+ *   global state and never allocates on these paths.
+ * - bf16 tensors are passed as raw bf16 bit patterns (uint16_t).
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Every call is asynchronous on `stream` and never synchronises it.
+ * - All arguments are validated on the host before anything is launched; on
+ *   failure a negative flux_status is returned and nothing is launched.  Data
+ *   that lives on the device (lengths, routes, mask rows) cannot be checked on
+ *   the host: kernels clamp it into range so that bad values give wrong
+ *   numbers, never out-of-bounds accesses.
+ * - A launch failure reported by the HIP runtime returns FLUX_ERR_HIP.
+ * - No C++ exception crosses this interface.
+ */
+#ifndef FLUX_H
+#define FLUX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLUX_OK = 0,
+  FLUX_ERR_INVALID_ARG = -1,  /* null pointer, bad size or inconsistent shapes */
+  FLUX_ERR_UNSUPPORTED = -2,  /* valid but not built (head_dim, block size ...) */
+  FLUX_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+  FLUX_ERR_HIP = -4           /* the HIP runtime reported an error */
+} flux_status;
+
+typedef enum { FLUX_F32 = 0, FLUX_BF16 = 1 } flux_dtype;
+
+/* Sparse Attention block pattern: block (i, j) of the mask is active iff
+ * j <= i and (j < sink_blocks or j >= i - local_blocks + 1).
+ * block_size in {64, 128}; sink_blocks >= 0; local_blocks >= 1 (counts the
+ * diagonal block, so no row is ever empty). */
+typedef struct {
+  int32_t block_size;
+  int32_t sink_blocks;
+  int32_t local_blocks;
+} flux_sa_params;
+
+/* Text for a status code [host]. */
+const char* flux_status_str(int32_t status);
+
+/*
+ * flux_route -- Layer Router: pooling, MLP and hard threshold.
+ * (technical summary, section 2: the router pools the first and last 100
+ * prompt tokens, an MLP context encoder maps them to a per-layer decision,
+ * and inference thresholds the soft weight to 0/1.)
+ *
+ * For each request r with S = cu_seqlens[r+1] - cu_seqlens[r] rows:
+ *   pooled = mean of hidden rows {0..min(100,S)-1} U {max(0,S-100)..S-1}
+ *            (a set: rows in both ends count once), accumulated in fp32;
+ *   z      = W2 * relu(W1 * pooled + b1) + b2       (fp32);
+ *   route[r][l] = 1 (FA) if z[l] >= 0 else 0 (SA)   (sigmoid(z) >= 0.5).
+ *
+ * hidden      [device] [T][d_in] rows of all requests packed back to back,
+ *             fp32 or bf16 per hidden_dtype (a flux_dtype value).
+ * cu_seqlens  [device] int32 [n_req+1], prefix offsets into the rows; each
+ *             request needs S >= 1 (S <= 0 yields pooled = 0).
+ * w1, b1      [device] fp32 [h1][d_in], [h1]     (PyTorch Linear layout)
+ * w2, b2      [device] fp32 [n_layers][h1], [n_layers]
+ * route_out   [device] uint8 [n_req][n_layers]
+ * logits_out  [device] fp32 [n_req][n_layers] or NULL
+ * Limits: 1 <= n_req, 1 <= d_in <= 8192, 1 <= h1 <= 4096, 1 <= n_layers <= 4096.
+ */
+flux_status flux_route(const void* hidden, int32_t hidden_dtype,
+                       const int32_t* cu_seqlens, int32_t n_req, int32_t d_in,
+                       const float* w1, const float* b1, int32_t h1,
+                       const float* w2, const float* b2, int32_t n_layers,
+                       uint8_t* route_out, float* logits_out, void* stream);
+
+/* Number of mask blocks for a sequence: ceil(seqlen / block_size) [host].
+ * Returns a negative flux_status on invalid input. */
+int64_t flux_mask_blocks(int32_t seqlen, flux_sa_params p);
+
+/* Active blocks of the mask for `seqlen` tokens, in closed form [host]:
+ * sum over rows i < nb of min(i+1, w) + max(0, min(s, i-w+1)).
+ * Returns a negative flux_status on invalid input. */
+int64_t flux_mask_nnz(int32_t seqlen, flux_sa_params p);
+
+/*
+ * flux_build_block_mask -- the SA block mask (integer, exact).
+ * SA layers run block-sparse attention (Block-Sparse-Attention library, named
+ * on the Flux Attention Qwen3-4B model card, "Sample Usage") and keep only a
+ * minimal KV set (technical summary, section 2); the block pattern is the
+ * sink + causal local window defined at flux_sa_params.
+ *
+ * With nb = flux_mask_blocks(seqlen, p) and nnz = flux_mask_nnz(seqlen, p):
+ * mask_out [device] uint8 [nb][nb] dense mask, or NULL to skip it;
+ * row_ptr  [device] int32 [nb+1];  col_idx [device] int32 [nnz], columns
+ *          strictly increasing within a row (what the attention kernels read).
+ * One mask built for the longest sequence serves every shorter one: entry
+ * (i, j) does not depend on the length.  1 <= seqlen, nb <= 65536.
+ */
+flux_status flux_build_block_mask(int32_t seqlen, flux_sa_params p, uint8_t* mask_out,
+                                  int32_t* row_ptr, int32_t* col_idx, void* stream);
+
+/*
+ * flux_attn_prefill -- one attention layer over a packed batch of prompts.
+ * FA: causal softmax attention; SA: the same restricted to the active blocks
+ * of the mask (abstract: each layer runs FA or SA; model card: SA is
+ * block-sparse attention).  For request r, query head h reads KV head
+ * h / (hq / hkv); key t is visible to query p iff t <= p and
+ * (route[r][layer] == 1 or block (p / B, t / B) is in the mask).
+ * Requests never attend to each other.  bf16 in/out, fp32 accumulation.
+ *
+ * q, out      [device] bf16 [T][hq][head_dim];  k, v [device] bf16 [T][hkv][head_dim]
+ * cu_seqlens  [device] int32 [n_req+1];  max_seqlen [host] >= every request length
+ * softmax_scale  > 0 (usually 1/sqrt(head_dim))
+ * route       [device] uint8 [n_req][n_layers], read at [r][layer]; 1 = FA
+ * mask_row_ptr, mask_col_idx  [device] CSR of flux_build_block_mask for
+ *             mask_blocks >= ceil(max_seqlen / block_size) rows; columns must
+ *             be increasing within a row.  Only read by SA layers.
+ * Supported: head_dim in {64, 128}, block_size in {64, 128}, hq % hkv == 0,
+ *            hq / hkv <= 16.  out may not alias q, k or v.
+ */
+flux_status flux_attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              uint16_t* out, const int32_t* cu_seqlens, int32_t n_req,
+                              int32_t max_seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
+                              float softmax_scale, const uint8_t* route, int32_t n_layers,
+                              int32_t layer, const int32_t* mask_row_ptr,
+                              const int32_t* mask_col_idx, int32_t mask_blocks,
+                              flux_sa_params p, void* stream);
+
+/* Workspace bytes flux_attn_decode needs for these sizes [host] (0 on invalid
+ * input). */
+size_t flux_attn_decode_workspace_size(int32_t n_seq, int32_t hq, int32_t hkv,
+                                       int32_t head_dim, int32_t max_len);
+
+/*
+ * flux_attn_decode -- one decode step of one layer, split-KV.
+ * The route fixed at prefill is reused for every decode step; SA layers read
+ * only the keys of their mask row and never the rest of the history
+ * (technical summary, section 2, deployment paragraph).
+ *
+ * Sequence b holds N = seqlens[b] keys in its cache, the newest token (the
+ * query's own) included, so the query is position N-1: FA reads keys
+ * 0..N-1; SA reads the keys of mask row (N-1) / block_size.
+ *
+ * q, out      [device] bf16 [n_seq][hq][head_dim]
+ * k_cache, v_cache [device] bf16 [n_seq][hkv][max_len][head_dim]
+ * seqlens     [device] int32 [n_seq], each in [1, max_len] (clamped on device)
+ * route       [device] uint8 [n_seq][n_layers], read at [b][layer]; 1 = FA
+ * mask_*      as for flux_attn_prefill, mask_blocks >= ceil(max_len / block_size)
+ * workspace   [device] >= flux_attn_decode_workspace_size(...) bytes, any
+ *             contents; it holds fp32 split partials between two kernels.
+ * Supported: head_dim in {64, 128}, block_size in {64, 128}, hq % hkv == 0,
+ *            hq / hkv <= 16.
+ */
+flux_status flux_attn_decode(const uint16_t* q, const uint16_t* k_cache,
+                             const uint16_t* v_cache, uint16_t* out, const int32_t* seqlens,
+                             int32_t n_seq, int32_t max_len, int32_t hq, int32_t hkv,
+                             int32_t head_dim, float softmax_scale, const uint8_t* route,
+                             int32_t n_layers, int32_t layer, const int32_t* mask_row_ptr,
+                             const int32_t* mask_col_idx, int32_t mask_blocks,
+                             flux_sa_params p, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLUX_H */

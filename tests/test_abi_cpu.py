@@ -1,0 +1,138 @@
+"""libflux C ABI on the host: the library loads, exports every symbol that
+include/flux.h declares, and its host-side functions and argument validation
+behave as documented.  No GPU work is launched: every validation case below
+fails before the library touches the HIP runtime."""
+
+import ctypes
+import re
+
+import pytest
+import torch
+
+import oracle
+from tests.flux_testlib import HEADER, LIB, ensure_built
+
+ensure_built()
+from block_sparse_attention_flux_amd import _lib  # noqa: E402
+
+lib = _lib.load()
+NULL = None
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation rejects the call first
+SA = _lib.SAParamsC
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(flux_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert len(syms) == 8, syms
+    raw = ctypes.CDLL(LIB)
+    for s in syms:
+        assert hasattr(raw, s), s
+    assert sorted(n for n, _, _ in _lib.SIGNATURES) == syms
+
+
+def test_status_strings():
+    assert lib.flux_status_str(0) == b"ok"
+    assert lib.flux_status_str(-1) == b"invalid argument"
+    assert lib.flux_status_str(-4) == b"HIP runtime error"
+    assert lib.flux_status_str(7) == b"unknown status"
+
+
+@pytest.mark.parametrize("seqlen,B,s,w", [(512, 64, 1, 2), (32768, 128, 1, 16), (131072, 128, 1, 32),
+                                          (1, 64, 0, 1), (1000, 128, 3, 2), (65536, 64, 0, 2000)])
+def test_mask_nnz_matches_oracle(seqlen, B, s, w):
+    nb = oracle.num_blocks(seqlen, B)
+    assert lib.flux_mask_blocks(seqlen, SA(B, s, w)) == nb
+    assert lib.flux_mask_nnz(seqlen, SA(B, s, w)) == oracle.mask_nnz(nb, s, w)
+
+
+def test_mask_host_validation():
+    assert lib.flux_mask_nnz(0, SA(64, 1, 2)) == _lib.FLUX_ERR_INVALID_ARG
+    assert lib.flux_mask_nnz(10, SA(64, 1, 0)) == _lib.FLUX_ERR_INVALID_ARG
+    assert lib.flux_mask_nnz(10, SA(64, -1, 1)) == _lib.FLUX_ERR_INVALID_ARG
+    assert lib.flux_mask_blocks(-5, SA(64, 1, 1)) == _lib.FLUX_ERR_INVALID_ARG
+    # builder: null outputs, bad params, unsupported block size, too many blocks
+    assert lib.flux_build_block_mask(512, SA(64, 1, 2), NULL, NULL, FAKE, NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert lib.flux_build_block_mask(512, SA(64, 1, 0), NULL, FAKE, FAKE, NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert lib.flux_build_block_mask(512, SA(32, 1, 2), NULL, FAKE, FAKE, NULL) == _lib.FLUX_ERR_UNSUPPORTED
+    assert lib.flux_build_block_mask(2**31 - 1, SA(64, 1, 2), NULL, FAKE, FAKE, NULL) == _lib.FLUX_ERR_UNSUPPORTED
+
+
+def test_route_validation():
+    args = dict(hidden=FAKE, dt=0, cu=FAKE, n_req=1, d_in=256, w1=FAKE, b1=FAKE, h1=64, w2=FAKE,
+                b2=FAKE, L=2, route=FAKE, logits=NULL, stream=NULL)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.flux_route(a["hidden"], a["dt"], a["cu"], a["n_req"], a["d_in"], a["w1"], a["b1"],
+                              a["h1"], a["w2"], a["b2"], a["L"], a["route"], a["logits"], a["stream"])
+    assert call(hidden=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(route=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(dt=5) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(n_req=0) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(L=0) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(d_in=8193) == _lib.FLUX_ERR_UNSUPPORTED
+    assert call(h1=5000) == _lib.FLUX_ERR_UNSUPPORTED
+
+
+PREFILL_OK = dict(q=FAKE, k=FAKE, v=ctypes.c_void_p(0x2000), out=ctypes.c_void_p(0x3000), cu=FAKE,
+                  n_req=1, max_seqlen=512, hq=4, hkv=2, d=64, scale=0.125, route=FAKE, L=2, layer=0,
+                  rp=FAKE, ci=FAKE, mb=8, sa=SA(64, 1, 2), stream=NULL)
+
+
+def prefill(**kw):
+    a = dict(PREFILL_OK, **kw)
+    return lib.flux_attn_prefill(a["q"], a["k"], a["v"], a["out"], a["cu"], a["n_req"], a["max_seqlen"],
+                                 a["hq"], a["hkv"], a["d"], a["scale"], a["route"], a["L"], a["layer"],
+                                 a["rp"], a["ci"], a["mb"], a["sa"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), -1), (dict(route=NULL), -1), (dict(rp=NULL), -1),
+    (dict(out=FAKE), -1),                      # out aliases q
+    (dict(hq=5, hkv=2), -1), (dict(hkv=0), -1), (dict(n_req=0), -1), (dict(max_seqlen=0), -1),
+    (dict(layer=2), -1), (dict(layer=-1), -1), (dict(scale=0.0), -1), (dict(scale=float("nan")), -1),
+    (dict(sa=SA(64, 1, 0)), -1), (dict(sa=SA(64, -2, 1)), -1),
+    (dict(mb=7), -1),                          # mask too small for max_seqlen
+    (dict(d=96), -2), (dict(sa=SA(32, 1, 2)), -2), (dict(hq=34, hkv=2), -2),
+])
+def test_prefill_validation(kw, code):
+    assert prefill(**kw) == code
+
+
+def test_decode_validation():
+    ws = lib.flux_attn_decode_workspace_size(16, 32, 8, 128, 32768)
+    assert ws > 0 and ws % 4 == 0
+    assert lib.flux_attn_decode_workspace_size(0, 32, 8, 128, 32768) == 0
+
+    def dec(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=ctypes.c_void_p(0x3000), sl=FAKE, n=16, ml=32768, hq=32,
+                 hkv=8, d=128, scale=0.088, route=FAKE, L=36, layer=0, rp=FAKE, ci=FAKE, mb=256,
+                 sa=SA(128, 1, 16), ws=FAKE, wsb=ws, stream=NULL)
+        a.update(kw)
+        return lib.flux_attn_decode(a["q"], a["k"], a["v"], a["out"], a["sl"], a["n"], a["ml"], a["hq"],
+                                    a["hkv"], a["d"], a["scale"], a["route"], a["L"], a["layer"], a["rp"],
+                                    a["ci"], a["mb"], a["sa"], a["ws"], a["wsb"], a["stream"])
+    assert dec(q=NULL) == -1
+    assert dec(out=FAKE) == -1
+    assert dec(mb=255) == -1
+    assert dec(layer=36) == -1
+    assert dec(d=80) == -2
+    assert dec(ws=NULL) == -3
+    assert dec(wsb=ws - 4) == -3
+
+
+def test_binding_rejects_host_tensors():
+    import block_sparse_attention_flux_amd as flux
+    x = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        flux.attn_prefill(x, x[:, :1].contiguous(), x[:, :1].contiguous(), torch.zeros(2, dtype=torch.int32),
+                          4, torch.ones(1, 1, dtype=torch.uint8), 0, torch.zeros(2, dtype=torch.int32),
+                          torch.zeros(1, dtype=torch.int32), flux.SAParams(64, 1, 1))
+    assert flux.mask_nnz(32768, flux.SAParams(128, 1, 16)) == 4216
+    with pytest.raises(ValueError):
+        flux.mask_nnz(0, flux.SAParams(128, 1, 16))
