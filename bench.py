@@ -163,11 +163,12 @@ def main():
         f"SA {sa_ms:.3f} ms ({sa_flops / sa_ms / 1e9:.1f} TF/s)  router+mask {router_mask_ms:.3f} ms")
 
     if args.copy_probe:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        # plain elementwise kernel with known traffic: reads 256 MiB, writes 256 MiB
+        src = torch.zeros(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.add(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        log("copy probe: 268435456 bytes read, 268435456 bytes written")
+        log("copy probe: add kernel reads 268435456 bytes and writes 268435456 bytes")
         del src, dst
 
     result = {
@@ -203,6 +204,11 @@ def main():
             "traffic": None,
         },
     }
+    tr = counted_traffic("prefill_kernel")
+    if tr is not None:
+        result["roofline"]["traffic"] = round(tr["per_launch_bytes"])
+        result["roofline"]["traffic_note"] = ("bytes per launch (mean of the FA and SA launch) from "
+                                              "profiles/hbm_traffic_32k.json")
     del hidden
     torch.cuda.empty_cache()
 
@@ -216,6 +222,19 @@ def main():
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def counted_traffic(kernel):
+    """HBM bytes measured by rocprofv3 counters for `kernel`, or None once the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_32k.json")
+    try:
+        rec = json.load(open(path))[kernel]
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec if hashlib.sha256(src).hexdigest() == rec["source_sha256"] else None
 
 
 def run_decode(args, flux, syn, dev, stream, log):
@@ -289,6 +308,10 @@ def run_decode(args, flux, syn, dev, stream, log):
                      "fa_layer_gbs": round(fa_gbs, 1),
                      "sa_layer_gbs": round(sa_bytes / sa_ms / 1e6, 1)},
     }
+    tr = counted_traffic("decode_split_kernel")
+    if tr is not None:
+        res["roofline"]["traffic"] = round(len(fa_layers) * tr["fa_bytes"] + len(sa_layers) * tr["sa_bytes"])
+        res["roofline"]["traffic_note"] = "bytes per decode step from profiles/hbm_traffic_32k.json"
     del kc, vc
     torch.cuda.empty_cache()
     return res
