@@ -11,19 +11,29 @@
 //   so inactive K/V tiles are never loaded.
 //
 // Per key tile and wave (bf16 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulate):
-//   S^T[key][q] = K Q^T      A = K tile from LDS, B = Q kept in registers
+//   S^T[key][q] = K Q^T      A = K rows from LDS, B = Q kept in registers
 //   online softmax in the log2 domain, row max across the two lane halves
-//   O^T[d][q] += V^T P^T     A = V^T from LDS (stored transposed), B = P
-//   Computing the transposed products puts one query row in each lane
-//   (q = lane % 32), so the softmax statistics and the O rescale are per-lane
-//   scalars and P lands directly in the B-operand layout of the second MFMA.
+//   O^T[d][q] += V^T P^T     A = V^T via the LDS transpose read, B = P
+//   The transposed products put one query row in each lane (q = lane % 32),
+//   so softmax statistics and the O rescale are per-lane scalars and P lands
+//   directly in the B-operand layout of the second MFMA.
 //
-// The running max is only moved when it grows by more than 2^8 (the final
-// normalisation divides by a sum taken with the same stale max, so the result
-// is unchanged in exact arithmetic), which skips almost every O rescale.
+// Data movement
+//   K and V tiles go global -> LDS directly (global_load_lds_dwordx4, no
+//   register staging), row-major with the 16-byte chunks of each row XOR
+//   swizzled; every LDS read below is bank-conflict free.  V^T operands come
+//   from ds_read_b64_tr_b16: within each 16-lane group, destination lane
+//   4i+j receives element j of source lanes i, i+4, i+8, i+12, so four source
+//   lanes pointing at four keys deliver those keys' values of one d column.
+//   K is fetched two tiles ahead and V one tile ahead (two LDS buffers each),
+//   which lets the wave issue tile n+1's K Q^T MFMAs while it runs tile n's
+//   softmax on the VALU.  One barrier per tile.
 //
-// Staging: K/V tiles go global -> registers -> LDS, double buffered, with the
-// loads of tile n+1 in flight while tile n is computed (one barrier per tile).
+// The running max is only moved when a row's max grows by more than 2^8 (the
+// final normalisation divides by a sum taken with the same stale max, so the
+// result is unchanged in exact arithmetic); rows that do not move scale by
+// exactly 1, so each row depends on its own data only.
+//
 // Workgroups are ordered so that each XCD (own L2) works through whole KV
 // head groups, heaviest causal rows first.
 #include "flux_device.h"
@@ -35,45 +45,31 @@ namespace {
 constexpr int BN = 64;                 // keys per tile
 constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag
 
-template <int D>
-struct Lds {
-  static constexpr int KPITCH = D * 2 + 16;   // bytes per K row (pad: conflict-free reads)
-  static constexpr int VPITCH = BN * 2 + 16;  // bytes per V^T row
-  static constexpr int KBYTES = BN * KPITCH;
-  static constexpr int VBYTES = D * VPITCH;
-  static constexpr int STAGE = KBYTES + VBYTES;
-};
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Position (in 4-key quads) of key quad kq inside a V^T row.  The B operand
-// slot i of lane half h in k-step ks holds key 16ks + 8(i/4) + 4h + i%4 (the
-// row order of the S^T accumulator); this permutation puts those 8 keys next
-// to each other so the A operand is one 16-byte read.
-__device__ __forceinline__ int quad_slot(int kq) {
-  return (kq & ~3) | ((kq & 1) << 1) | ((kq >> 1) & 1);
-}
-// XOR swizzle of quad positions by the d-chunk (keeps 16-byte pairs intact).
-__device__ __forceinline__ int quad_swz(int d) { return ((d >> 3) & 7) << 1; }
+// XOR swizzle of a row's 16-byte chunks: rows r..r+7 map a fixed chunk to 8
+// different bank groups, and rows {4h+m} map a chunk pair to 8 distinct ones.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
-// bf16 element e (0 = low half, 1 = high half) of dwords a and b, packed as
-// (a.e, b.e): one column of two consecutive key rows.
-__device__ __forceinline__ uint32_t pick_pair(uint32_t a, uint32_t b, int e) {
-  return e ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-}
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 template <int D, int BM>
 __global__ __launch_bounds__(BM * 2, 2) void prefill_kernel(const PrefillParams p) {
-  constexpr int NT = BM * 2;          // threads
-  constexpr int KS = D / 16;          // k-steps of K Q^T
-  constexpr int DT = D / 32;          // 32-row tiles of O^T
-  constexpr int TPB = BM / BN;        // key tiles per mask block
-  constexpr int CH = D / 8;           // 16-byte chunks per row
-  constexpr int KLOADS = BN * CH / NT;
-  constexpr int NQC = (BN / 4) * CH;  // (key quad, chunk) pairs of a V tile
-  constexpr int VLOADS = (NQC + NT - 1) / NT;
-  using L = Lds<D>;
-  static_assert(BN * CH % NT == 0, "K tile must split evenly over the threads");
-
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * L::STAGE];
+  constexpr int NT = BM * 2;           // threads
+  constexpr int KS = D / 16;           // k-steps of K Q^T
+  constexpr int DT = D / 32;           // 32-row tiles of O^T
+  constexpr int TPB = BM / BN;         // key tiles per mask block
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int ROWB = D * 2;          // bytes per K/V row in LDS
+  constexpr int TILEB = BN * ROWB;     // bytes per K or V tile
+  constexpr int LOADS = TILEB / (NT * 16);
+  static_assert(TILEB % (NT * 16) == 0, "tile must split into whole wave loads");
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[4 * TILEB];  // K0 K1 V0 V1
+  lds_u8* lds = (lds_u8*)(lds_raw);  // the same array, addressed as LDS
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
@@ -115,9 +111,27 @@ __global__ __launch_bounds__(BM * 2, 2) void prefill_kernel(const PrefillParams 
     while (n_tiles > 0 && tile_start(n_tiles - 1) >= q_end) --n_tiles;
   }
 
+  // ---- global -> LDS tile loads: thread slot s = j*NT + tid holds row s/CH,
+  // chunk slot s%CH, which stores global chunk (s%CH) ^ swz(row).
   const size_t kv_row = static_cast<size_t>(p.hkv) * D;  // elements per token in k/v
   const uint16_t* kbase = p.k + static_cast<size_t>(tok0) * kv_row + static_cast<size_t>(g) * D;
   const uint16_t* vbase = p.v + static_cast<size_t>(tok0) * kv_row + static_cast<size_t>(g) * D;
+  int ld_row[LOADS], ld_col[LOADS];
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int s = j * NT + tid;
+    ld_row[j] = s / CH;
+    ld_col[j] = ((s % CH) ^ swz(s / CH)) * 8;
+  }
+  auto issue_tile = [&](const uint16_t* base, int kst, int buf) {
+    lds_u8* dst0 = lds + buf * TILEB + wave * 64 * 16;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int key = min(kst + ld_row[j], S - 1);  // rows past the end: any finite row, masked later
+      const uint16_t* src = base + static_cast<size_t>(key) * kv_row + ld_col[j];
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<lds_void*>(dst0 + j * NT * 16), 16, 0, 0);
+    }
+  };
 
   // ---- Q^T operand, kept in registers for the whole key loop
   const int row = q0 + wave * 32 + l32;
@@ -133,63 +147,13 @@ __global__ __launch_bounds__(BM * 2, 2) void prefill_kernel(const PrefillParams 
     }
   }
 
-  // ---- staging registers
-  u32x4 kreg[KLOADS];
-  u32x4 vreg[VLOADS][4];
+  // per-lane operand coordinates
+  //   K A operand: row key = mt*32 + l32, chunk 2ks + half
+  //   V^T A operand (transpose read): source lane s = lane%16 points at key
+  //   16ks + 8a + 4*half + s/4 and d = 32dt + 16*((lane/16)%2) + 4*(s%4)
+  const int vt_key0 = 4 * half + ((lane & 15) >> 2);          // + 16ks + 8a
+  const int vt_d0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32dt
 
-  auto load_tile = [&](int ks0) {
-#pragma unroll
-    for (int j = 0; j < KLOADS; ++j) {
-      const int id = tid + NT * j;
-      const int r = id / CH, c = id % CH;
-      const int key = ks0 + r;
-      kreg[j] = key < S ? ld16(kbase + static_cast<size_t>(key) * kv_row + c * 8)
-                        : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < VLOADS; ++j) {
-      const int id = tid + NT * j;
-      if (NQC % NT == 0 || id < NQC) {
-        const int c = id % CH, qd = id / CH;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int key = ks0 + qd * 4 + kk;
-          vreg[j][kk] = key < S ? ld16(vbase + static_cast<size_t>(key) * kv_row + c * 8)
-                                : u32x4{0, 0, 0, 0};
-        }
-      }
-    }
-  };
-
-  auto store_tile = [&](int stage) {
-    unsigned char* kl = lds + stage * L::STAGE;
-    unsigned char* vl = kl + L::KBYTES;
-#pragma unroll
-    for (int j = 0; j < KLOADS; ++j) {
-      const int id = tid + NT * j;
-      const int r = id / CH, c = id % CH;
-      *reinterpret_cast<u32x4*>(kl + r * L::KPITCH + c * 16) = kreg[j];
-    }
-#pragma unroll
-    for (int j = 0; j < VLOADS; ++j) {
-      const int id = tid + NT * j;
-      if (NQC % NT == 0 || id < NQC) {
-        const int c = id % CH, qd = id / CH;
-        const int slot = quad_slot(qd);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int d = c * 8 + i;
-          const int dw = i >> 1;
-          const uint32_t lo = pick_pair(vreg[j][0][dw], vreg[j][1][dw], i & 1);
-          const uint32_t hi2 = pick_pair(vreg[j][2][dw], vreg[j][3][dw], i & 1);
-          *reinterpret_cast<u32x2*>(vl + d * L::VPITCH + ((slot ^ quad_swz(d)) * 8)) =
-              u32x2{lo, hi2};
-        }
-      }
-    }
-  };
-
-  // ---- per-wave softmax state and output accumulator
   const float cs = p.scale * kLog2e;  // scores -> log2 domain
   float m_run = kNegInf, l_run = 0.0f;
   f32x16 oacc[DT];
@@ -197,25 +161,32 @@ __global__ __launch_bounds__(BM * 2, 2) void prefill_kernel(const PrefillParams 
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
 
   const int wrow0 = q0 + wave * 32;
-  const bool wave_live = wrow0 < S;
+  // tiles this wave must see: every tile up to the last one starting at or before its last row
+  int n_mine = 0;
+  if (wrow0 < S) {
+    n_mine = n_tiles;
+    while (n_mine > 0 && tile_start(n_mine - 1) > wrow0 + 31) --n_mine;
+  }
 
-  auto compute_tile = [&](int stage, int kst) {
-    if (!wave_live || kst > wrow0 + 31) return;  // nothing visible to this wave
-    const unsigned char* kl = lds + stage * L::STAGE;
-    const unsigned char* vl = kl + L::KBYTES;
-
-    f32x16 sacc[2];
+  auto qk = [&](int kbuf, f32x16 (&sacc)[2]) {
+    const lds_u8* kl = lds + kbuf * TILEB;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       sacc[mt] = f32x16{};
-      const unsigned char* kp = kl + (mt * 32 + l32) * L::KPITCH + half * 16;
+      const int key = mt * 32 + l32;
+      const lds_u8* kp = kl + key * ROWB;
+      const int sw = swz(key);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + ks * 32));
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[mt], 0, 0, 0);
+        const u32x4 raw = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            kp + (((2 * ks + half) ^ sw) << 4));
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(raw), qreg[ks], sacc[mt], 0, 0, 0);
       }
     }
+  };
 
+  // softmax of one S^T tile -> packed bf16 P (B operand layout), updates m/l/O
+  auto softmax = [&](f32x16 (&sacc)[2], int kst, uint32_t (&pk)[16]) {
     if (kst + BN - 1 > wrow0) {  // tile crosses the diagonal: causal mask
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -225,7 +196,6 @@ __global__ __launch_bounds__(BM * 2, 2) void prefill_kernel(const PrefillParams 
           if (key > row) sacc[mt][r] = kNegInf;
         }
     }
-
     float mx = kNegInf;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -233,9 +203,6 @@ __global__ __launch_bounds__(BM * 2, 2) void prefill_kernel(const PrefillParams 
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
     mx = fmaxf(mx, xor32(mx));
     const float mxs = mx * cs;
-    // Rows whose max grew past the slack move their max; every other row keeps
-    // it and scales by exactly 1, so each row's result depends on its own data
-    // only.  The multiply is skipped when no row of the wave moved.
     const bool grow = mxs > m_run + kRescaleSlack;
     if (__ballot(grow) != 0) {
       const float m_new = grow ? mxs : m_run;
@@ -246,8 +213,6 @@ __global__ __launch_bounds__(BM * 2, 2) void prefill_kernel(const PrefillParams 
       m_run = m_new;
     }
     const float mu = (m_run == kNegInf) ? 0.0f : m_run;
-
-    uint32_t pk[16];
     float psum = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -259,36 +224,59 @@ __global__ __launch_bounds__(BM * 2, 2) void prefill_kernel(const PrefillParams 
         pk[mt * 8 + r / 2] = pack_bf16x2(p0, p1);
       }
     l_run += psum;
+  };
 
+  auto vt_read = [&](const lds_u8* vl, int key, int d) -> s16x4 {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(
+        const_cast<lds_u8*>(vl) + key * ROWB + ((((d >> 3) ^ swz(key)) << 4) | ((d & 7) << 1))));
+  };
+
+  auto pv = [&](int vbuf, const uint32_t (&pk)[16]) {
+    const lds_u8* vl = lds + (2 + vbuf) * TILEB;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = dt * 32 + l32;
-      const unsigned char* vp = vl + d * L::VPITCH;
-      const int swz = quad_swz(d);
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 b = as_bf16x8(u32x4{pk[ks * 4], pk[ks * 4 + 1], pk[ks * 4 + 2], pk[ks * 4 + 3]});
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int u = ks * 4 + half * 2;
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(vp + (u ^ swz) * 8));
-        const bf16x8 b = as_bf16x8(u32x4{pk[ks * 4], pk[ks * 4 + 1], pk[ks * 4 + 2], pk[ks * 4 + 3]});
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, oacc[dt], 0, 0, 0);
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = dt * 32 + vt_d0;
+        const s16x4 lo = vt_read(vl, ks * 16 + vt_key0, d);
+        const s16x4 hi4 = vt_read(vl, ks * 16 + 8 + vt_key0, d);
+        const s16x8 a8 = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), b, oacc[dt],
+                                                           0, 0, 0);
       }
     }
   };
 
-  // ---- key loop: tile n computed from LDS while tile n+1 is in flight
+  // ---- key loop.  Iteration n: loads of K_{n+2}, V_{n+1} in flight; S_{n+1}
+  // computed while tile n's softmax runs; then O += V_n P_n.
   if (n_tiles > 0) {
-    int kst = tile_start(0);
-    load_tile(kst);
-    store_tile(0);
+    const int kst0 = tile_start(0);
+    int kst_nxt = n_tiles > 1 ? tile_start(1) : 0;
+    issue_tile(kbase, kst0, 0);
+    issue_tile(vbase, kst0, 2);
+    if (n_tiles > 1) issue_tile(kbase, kst_nxt, 1);
+    wait_vmem();
     __syncthreads();
+    f32x16 s_cur[2], s_nxt[2];
+    if (n_mine > 0) qk(0, s_cur);
+    int kst_cur = kst0;
     for (int n = 0; n < n_tiles; ++n) {
-      const bool more = n + 1 < n_tiles;
-      const int kst_next = more ? tile_start(n + 1) : 0;
-      if (more) load_tile(kst_next);
-      compute_tile(n & 1, kst);
-      if (more) store_tile((n + 1) & 1);
+      const int kst_n2 = n + 2 < n_tiles ? tile_start(n + 2) : 0;
+      if (n + 2 < n_tiles) issue_tile(kbase, kst_n2, n & 1);
+      if (n + 1 < n_tiles) issue_tile(vbase, kst_nxt, 2 + ((n + 1) & 1));
+      if (n < n_mine) {
+        uint32_t pk[16];
+        if (n + 1 < n_mine) qk((n + 1) & 1, s_nxt);
+        softmax(s_cur, kst_cur, pk);
+        pv(n & 1, pk);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) s_cur[mt] = s_nxt[mt];
+      }
+      wait_vmem();
       __syncthreads();
-      kst = kst_next;
+      kst_cur = kst_nxt;
+      kst_nxt = kst_n2;
     }
   }
 
