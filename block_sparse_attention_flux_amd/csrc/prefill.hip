@@ -1,11 +1,11 @@
-// Routed prefill attention for gfx950: one kernel serves Full Attention (FA)
-// and block-Sparse Attention (SA) layers; the layer's mode is read from the
-// route vector on the device (Flux Attention abstract: a router sends each
-// layer to FA or SA; technical summary on gist.science, section 2).
+// Routed prefill attention for gfx950: one kernel family serves Full
+// Attention (FA) and block-Sparse Attention (SA) layers; the layer's mode is
+// read from the route vector on the device (Flux Attention abstract: a router
+// sends each layer to FA or SA; technical summary on gist.science, section 2).
 //
 // Work decomposition
-//   One workgroup = one query block of BM rows (BM = the mask block size, 64
-//   or 128) of one query head of one request; BM/32 waves of 32 rows each.
+//   A workgroup owns one query block of BM rows (BM = the mask block size, 64
+//   or 128) of one request.  Each wave owns 32 query rows of one query head.
 //   Key tiles of BN = 64 keys.  FA visits every tile up to the diagonal; SA
 //   visits only the tiles of the blocks listed in the query block's CSR row,
 //   so inactive K/V tiles are never loaded.
@@ -16,18 +16,29 @@
 //   O^T[d][q] += V^T P^T     A = V^T via the LDS transpose read, B = P
 //   The transposed products put one query row in each lane (q = lane % 32),
 //   so softmax statistics and the O rescale are per-lane scalars and P lands
-//   directly in the B-operand layout of the second MFMA.
+//   directly in the B-operand layout of the second MFMA.  Each product issues
+//   all of its LDS operand reads before its MFMAs so the reads overlap.
 //
 // Data movement
 //   K and V tiles go global -> LDS directly (global_load_lds_dwordx4, no
-//   register staging), row-major with the 16-byte chunks of each row XOR
-//   swizzled; every LDS read below is bank-conflict free.  V^T operands come
-//   from ds_read_b64_tr_b16: within each 16-lane group, destination lane
-//   4i+j receives element j of source lanes i, i+4, i+8, i+12, so four source
-//   lanes pointing at four keys deliver those keys' values of one d column.
-//   K is fetched two tiles ahead and V one tile ahead (two LDS buffers each),
-//   which lets the wave issue tile n+1's K Q^T MFMAs while it runs tile n's
-//   softmax on the VALU.  One barrier per tile.
+//   register staging): K row-major with XOR-swizzled 16-byte chunks, V in
+//   128-byte blocks of 4 keys x 16 d; every LDS read below is bank-conflict
+//   free.  V^T operands come from ds_read_b64_tr_b16: within each 16-lane
+//   group, destination lane 4i+j receives element j of source lanes i, i+4,
+//   i+8, i+12, so four source lanes pointing at four keys deliver those keys'
+//   values of one d column.
+//
+// Two kernels
+//   pair kernel (query heads per KV head even, the common GQA case): 2*BM/32
+//     waves = two query heads of the same KV group over the same rows, so
+//     every K/V tile in LDS feeds twice the waves.  The two head groups run
+//     half a tile apart: while one group does K Q^T + softmax (MFMA + VALU),
+//     the other does its P V MFMAs, and they swap at the next barrier, so the
+//     two waves that share a SIMD keep its matrix core and its VALU busy at
+//     the same time.  K and V loads alternate per half step and each gets a
+//     whole tile of latency cover.
+//   single kernel (odd group sizes): BM/32 waves of one head, K/V of the
+//     next tile loaded while the current one is computed.
 //
 // The running max is only moved when a row's max grows by more than 2^8 (the
 // final normalisation divides by a sum taken with the same stale max, so the
@@ -42,154 +53,176 @@
 namespace flux {
 namespace {
 
-constexpr int BN = 64;                 // keys per tile
+constexpr int kBN = 32;                // keys per tile
+constexpr int kOcc = 3;                // waves per SIMD the kernel is built for
 constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// XOR swizzle of a row's 16-byte chunks: rows r..r+7 map a fixed chunk to 8
-// different bank groups, and rows {4h+m} map a chunk pair to 8 distinct ones.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// LDS layouts (64 banks of 4 bytes; a 16-byte read is served 16 lanes per
+// pass, an 8-byte read 32 lanes per pass):
+//   K tile: row-major, 16-byte chunk c of row r stored at chunk slot
+//           c ^ (r % CH): the 16 rows read by one pass of the K operand read
+//           land in 16 different slots, i.e. all 64 banks.
+//   V tile: 128-byte blocks of 4 keys x 16 d, block (key/4, d/16), inside a
+//           block key-major then d.  A transpose read of one 16-lane group
+//           covers exactly one block, and a 32-lane pass two adjacent blocks.
+template <int CH>
+__device__ __forceinline__ int kslot(int row, int chunk) { return chunk ^ (row & (CH - 1)); }
 
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// vmcnt(N): wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
-template <int D, int BM>
-__global__ __launch_bounds__(BM * 2, 2) void prefill_kernel(const PrefillParams p) {
-  constexpr int NT = BM * 2;           // threads
-  constexpr int KS = D / 16;           // k-steps of K Q^T
-  constexpr int DT = D / 32;           // 32-row tiles of O^T
-  constexpr int TPB = BM / BN;         // key tiles per mask block
-  constexpr int CH = D / 8;            // 16-byte chunks per row
-  constexpr int ROWB = D * 2;          // bytes per K/V row in LDS
-  constexpr int TILEB = BN * ROWB;     // bytes per K or V tile
-  constexpr int LOADS = TILEB / (NT * 16);
+// Loads of one K or V tile into LDS by NT threads.  Load j of thread tid
+// fills LDS slot s = j*NT + tid (16 bytes, lane-linear per wave instruction);
+// the global chunk it fetches is chosen so that the slot ends up where the
+// layout wants it.  K: slot s is row s/CH, chunk slot s%CH.  V: slot s is
+// block s/8 = (key quad, d block), key 4*quad + (s%8)/2, chunk 2*dblk + s%2.
+template <int D, int NT, int BN>
+struct TileLoader {
+  static constexpr int CH = D / 8;
+  static constexpr int TILEB = BN * D * 2;
+  static constexpr int LOADS = TILEB / (NT * 16);
   static_assert(TILEB % (NT * 16) == 0, "tile must split into whole wave loads");
-  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[4 * TILEB];  // K0 K1 V0 V1
-  lds_u8* lds = (lds_u8*)(lds_raw);  // the same array, addressed as LDS
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, half = lane >> 5;
+  const unsigned char* kbase;
+  const unsigned char* vbase;
+  uint32_t row_bytes;
+  int S, tid, wave_u;
+  uint32_t koff[LOADS], voff[LOADS];
 
-  // ---- work item: XCD-major, then (kv group, query block heaviest first, request, head)
-  const int group = p.hq / p.hkv;
-  const int n_qt = (p.max_seqlen + BM - 1) / BM;
-  const int G = gridDim.x, bid = blockIdx.x;
-  int w = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-  const int hi = w % group;
-  w /= group;
-  const int req = w % p.n_req;
-  w /= p.n_req;
-  const int t = n_qt - 1 - (w % n_qt);
-  const int g = w / n_qt;
-  const int head = g * group + hi;
-
-  const int tok0 = p.cu_seqlens[req];
-  const int S = p.cu_seqlens[req + 1] - tok0;
-  const int q0 = t * BM;
-  if (q0 >= S) return;
-  const int q_end = min(q0 + BM, S);
-  const bool fa = p.route[static_cast<int64_t>(req) * p.n_layers + p.layer] != 0;
-
-  int rp0 = 0, n_tiles;
-  const int mrow = min(t, p.mask_blocks - 1);
-  if (fa) {
-    n_tiles = (q_end + BN - 1) / BN;
-  } else {
-    rp0 = p.row_ptr[mrow];
-    n_tiles = max(p.row_ptr[mrow + 1] - rp0, 0) * TPB;
-  }
-  auto tile_start = [&](int n) -> int {
-    if (fa) return n * BN;
-    const int blk = min(max(p.col_idx[rp0 + n / TPB], 0), t);
-    return blk * BM + (n % TPB) * BN;
-  };
-  if (!fa) {
-    while (n_tiles > 0 && tile_start(n_tiles - 1) >= q_end) --n_tiles;
-  }
-
-  // ---- global -> LDS tile loads: thread slot s = j*NT + tid holds row s/CH,
-  // chunk slot s%CH, which stores global chunk (s%CH) ^ swz(row).
-  const size_t kv_row = static_cast<size_t>(p.hkv) * D;  // elements per token in k/v
-  const uint16_t* kbase = p.k + static_cast<size_t>(tok0) * kv_row + static_cast<size_t>(g) * D;
-  const uint16_t* vbase = p.v + static_cast<size_t>(tok0) * kv_row + static_cast<size_t>(g) * D;
-  int ld_row[LOADS], ld_col[LOADS];
-#pragma unroll
-  for (int j = 0; j < LOADS; ++j) {
+  __device__ __forceinline__ void k_src(int j, int& r, int& c) const {
     const int s = j * NT + tid;
-    ld_row[j] = s / CH;
-    ld_col[j] = ((s % CH) ^ swz(s / CH)) * 8;
+    r = s / CH;
+    c = kslot<CH>(s / CH, s % CH);
   }
-  auto issue_tile = [&](const uint16_t* base, int kst, int buf) {
-    lds_u8* dst0 = lds + buf * TILEB + wave * 64 * 16;
+  __device__ __forceinline__ void v_src(int j, int& r, int& c) const {
+    const int s = j * NT + tid;
+    const int blk = s / 8, kq = blk / (D / 16), dblk = blk % (D / 16);
+    r = 4 * kq + (s % 8) / 2;
+    c = 2 * dblk + (s % 2);
+  }
+  __device__ __forceinline__ void init(const uint16_t* k, const uint16_t* v, int tok0, int hkv, int g,
+                                       int seqlen, int thread) {
+    const size_t kv_row = static_cast<size_t>(hkv) * D;
+    row_bytes = static_cast<uint32_t>(kv_row * 2);
+    kbase = reinterpret_cast<const unsigned char*>(k + static_cast<size_t>(tok0) * kv_row +
+                                                   static_cast<size_t>(g) * D);
+    vbase = reinterpret_cast<const unsigned char*>(v + static_cast<size_t>(tok0) * kv_row +
+                                                   static_cast<size_t>(g) * D);
+    S = seqlen;
+    tid = thread;
+    wave_u = __builtin_amdgcn_readfirstlane(thread >> 6);
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      const int key = min(kst + ld_row[j], S - 1);  // rows past the end: any finite row, masked later
-      const uint16_t* src = base + static_cast<size_t>(key) * kv_row + ld_col[j];
-      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<lds_void*>(dst0 + j * NT * 16), 16, 0, 0);
+      int r, c;
+      k_src(j, r, c);
+      koff[j] = r * row_bytes + c * 16;
+      v_src(j, r, c);
+      voff[j] = r * row_bytes + c * 16;
     }
-  };
+  }
+  // Issue the loads of the tile starting at key kst into LDS at `dst`.
+  __device__ __forceinline__ void issue(bool is_v, int kst, lds_u8* dst) const {
+    const unsigned char* base = is_v ? vbase : kbase;
+    lds_u8* dst0 = dst + wave_u * 64 * 16;
+    if (kst + BN <= S) {
+      const unsigned char* sb = base + static_cast<size_t>(kst) * row_bytes;  // uniform
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(sb + (is_v ? voff[j] : koff[j])),
+                                         reinterpret_cast<lds_void*>(dst0 + j * NT * 16), 16, 0, 0);
+    } else {  // last tile of the sequence: rows past the end read the last row (masked later)
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) {
+        int r, c;
+        if (is_v) v_src(j, r, c); else k_src(j, r, c);
+        const int key = min(kst + r, S - 1);
+        __builtin_amdgcn_global_load_lds(
+            static_cast<const void*>(base + static_cast<size_t>(key) * row_bytes + c * 16),
+            reinterpret_cast<lds_void*>(dst0 + j * NT * 16), 16, 0, 0);
+      }
+    }
+  }
+};
 
-  // ---- Q^T operand, kept in registers for the whole key loop
-  const int row = q0 + wave * 32 + l32;
-  const bool row_ok = row < S;
+// Per-wave state and math for 32 query rows of one head.
+template <int D, int BN>
+struct WaveAttn {
+  static constexpr int KS = D / 16;   // k-steps of K Q^T
+  static constexpr int DT = D / 32;   // 32-row tiles of O^T
+  static constexpr int CH = D / 8;
+  static constexpr int ROWB = D * 2;
+  static constexpr int MT = BN / 32;  // 32-key tiles of S^T
+  static constexpr int PK = BN / 4;   // packed bf16 pairs of P per lane
+
   bf16x8 qreg[KS];
-  {
+  f32x16 oacc[DT];
+  float m_run, l_run, cs;
+  int row, wrow0, half, l32, vt_blk0, vt_in;
+
+  __device__ __forceinline__ void init(const uint16_t* q, int tok0, int hq, int head, int q_row0,
+                                       int S, float scale, int lane) {
+    l32 = lane & 31;
+    half = lane >> 5;
+    wrow0 = q_row0;
+    row = q_row0 + l32;
+    const bool row_ok = row < S;
     const uint16_t* qp =
-        p.q + (static_cast<size_t>(tok0 + (row_ok ? row : 0)) * p.hq + head) * D + half * 8;
+        q + (static_cast<size_t>(tok0 + (row_ok ? row : 0)) * hq + head) * D + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = row_ok ? ld16(qp + ks * 16) : u32x4{0, 0, 0, 0};
       qreg[ks] = as_bf16x8(v);
     }
+    cs = scale * kLog2e;  // scores -> log2 domain
+    m_run = kNegInf;
+    l_run = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+    // V^T A operand (transpose read): source lane s = lane%16 points at key
+    // 16ks + 8a + 4*half + s/4 and d = 32dt + 16*((lane/16)%2) + 4*(s%4), i.e.
+    // block (4ks + 2a + half, 2dt + (lane/16)%2), byte (s/4)*32 + (s%4)*8
+    vt_blk0 = half * (D / 16) + ((lane >> 4) & 1);
+    vt_in = ((lane & 15) >> 2) * 32 + (lane & 3) * 8;
   }
 
-  // per-lane operand coordinates
-  //   K A operand: row key = mt*32 + l32, chunk 2ks + half
-  //   V^T A operand (transpose read): source lane s = lane%16 points at key
-  //   16ks + 8a + 4*half + s/4 and d = 32dt + 16*((lane/16)%2) + 4*(s%4)
-  const int vt_key0 = 4 * half + ((lane & 15) >> 2);          // + 16ks + 8a
-  const int vt_d0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32dt
-
-  const float cs = p.scale * kLog2e;  // scores -> log2 domain
-  float m_run = kNegInf, l_run = 0.0f;
-  f32x16 oacc[DT];
+  // S^T for the 64 keys of the K tile at kl: A = key row mt*32 + l32, chunk 2ks + half
+  __device__ __forceinline__ void qk(const lds_u8* kl, f32x16 (&sacc)[MT]) const {
+    u32x4 kop[MT][KS];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
-
-  const int wrow0 = q0 + wave * 32;
-  // tiles this wave must see: every tile up to the last one starting at or before its last row
-  int n_mine = 0;
-  if (wrow0 < S) {
-    n_mine = n_tiles;
-    while (n_mine > 0 && tile_start(n_mine - 1) > wrow0 + 31) --n_mine;
-  }
-
-  auto qk = [&](int kbuf, f32x16 (&sacc)[2]) {
-    const lds_u8* kl = lds + kbuf * TILEB;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      sacc[mt] = f32x16{};
+    for (int mt = 0; mt < MT; ++mt) {
       const int key = mt * 32 + l32;
       const lds_u8* kp = kl + key * ROWB;
-      const int sw = swz(key);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 raw = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-            kp + (((2 * ks + half) ^ sw) << 4));
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(raw), qreg[ks], sacc[mt], 0, 0, 0);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        kop[mt][ks] = *reinterpret_cast<const lds_u32x4*>(kp + (kslot<CH>(key, 2 * ks + half) << 4));
     }
-  };
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      sacc[mt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[mt][ks]), qreg[ks], sacc[mt],
+                                                           0, 0, 0);
+    }
+  }
 
-  // softmax of one S^T tile -> packed bf16 P (B operand layout), updates m/l/O
-  auto softmax = [&](f32x16 (&sacc)[2], int kst, uint32_t (&pk)[16]) {
+  // Causal mask, row max, lazy rescale, exponentials -> packed bf16 P
+  __device__ __forceinline__ void softmax(f32x16 (&sacc)[MT], int kst, uint32_t (&pk)[PK]) {
     if (kst + BN - 1 > wrow0) {  // tile crosses the diagonal: causal mask
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kst + mt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
@@ -198,11 +231,13 @@ __global__ __launch_bounds__(BM * 2, 2) void prefill_kernel(const PrefillParams 
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
     mx = fmaxf(mx, xor32(mx));
     const float mxs = mx * cs;
+    // Rows whose max grew past the slack move their max; every other row keeps
+    // it and scales by exactly 1.  The multiply is skipped when no row moved.
     const bool grow = mxs > m_run + kRescaleSlack;
     if (__ballot(grow) != 0) {
       const float m_new = grow ? mxs : m_run;
@@ -215,7 +250,7 @@ __global__ __launch_bounds__(BM * 2, 2) void prefill_kernel(const PrefillParams 
     const float mu = (m_run == kNegInf) ? 0.0f : m_run;
     float psum = 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(__builtin_fmaf(sacc[mt][r], cs, -mu));
@@ -224,84 +259,172 @@ __global__ __launch_bounds__(BM * 2, 2) void prefill_kernel(const PrefillParams 
         pk[mt * 8 + r / 2] = pack_bf16x2(p0, p1);
       }
     l_run += psum;
-  };
+  }
 
-  auto vt_read = [&](const lds_u8* vl, int key, int d) -> s16x4 {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(
-        const_cast<lds_u8*>(vl) + key * ROWB + ((((d >> 3) ^ swz(key)) << 4) | ((d & 7) << 1))));
-  };
+  __device__ __forceinline__ s16x4 vt_read(const lds_u8* vl, int blk) const {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_s16x4*>(const_cast<lds_u8*>(vl) + blk * 128 + vt_in));
+  }
 
-  auto pv = [&](int vbuf, const uint32_t (&pk)[16]) {
-    const lds_u8* vl = lds + (2 + vbuf) * TILEB;
+  // O^T += V^T P^T for the V tile at vl
+  __device__ __forceinline__ void pv(const lds_u8* vl, const uint32_t (&pk)[PK]) {
+    constexpr int PKS = BN / 16;  // k-steps of P V
+    s16x8 vop[PKS][DT];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 b = as_bf16x8(u32x4{pk[ks * 4], pk[ks * 4 + 1], pk[ks * 4 + 2], pk[ks * 4 + 3]});
+    for (int ks = 0; ks < PKS; ++ks)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int d = dt * 32 + vt_d0;
-        const s16x4 lo = vt_read(vl, ks * 16 + vt_key0, d);
-        const s16x4 hi4 = vt_read(vl, ks * 16 + 8 + vt_key0, d);
-        const s16x8 a8 = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), b, oacc[dt],
-                                                           0, 0, 0);
+        const int blk = vt_blk0 + 4 * ks * (D / 16) + 2 * dt;
+        const s16x4 lo = vt_read(vl, blk);                  // keys 16ks + 4*half + m
+        const s16x4 hi4 = vt_read(vl, blk + 2 * (D / 16));  // keys 16ks + 8 + 4*half + m
+        vop[ks][dt] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
       }
+#pragma unroll
+    for (int ks = 0; ks < PKS; ++ks) {
+      const bf16x8 b = as_bf16x8(u32x4{pk[ks * 4], pk[ks * 4 + 1], pk[ks * 4 + 2], pk[ks * 4 + 3]});
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[ks][dt]), b,
+                                                           oacc[dt], 0, 0, 0);
     }
-  };
+  }
 
-  // ---- key loop.  Iteration n: loads of K_{n+2}, V_{n+1} in flight; S_{n+1}
-  // computed while tile n's softmax runs; then O += V_n P_n.
+  // O = O^T / l, one query row per lane, 4 consecutive d per store
+  __device__ __forceinline__ void store(uint16_t* out, int tok0, int hq, int head, int S) const {
+    const float lt = l_run + xor32(l_run);
+    if (row < S) {
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      uint16_t* op = out + (static_cast<size_t>(tok0 + row) * hq + head) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d0 = dt * 32 + j * 8 + half * 4;
+          const uint32_t lo = pack_bf16x2(oacc[dt][j * 4] * inv, oacc[dt][j * 4 + 1] * inv);
+          const uint32_t hi2 = pack_bf16x2(oacc[dt][j * 4 + 2] * inv, oacc[dt][j * 4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + d0) = u32x2{lo, hi2};
+        }
+    }
+  }
+};
+
+// Query block's key tiles: FA = every tile up to the diagonal, SA = the
+// tiles of the blocks in the CSR row (columns clamped into [0, t]).
+template <int BM, int BN>
+struct TileList {
+  static constexpr int TPB = BM / BN;  // key tiles per mask block
+  const int32_t* col_idx;
+  int rp0, n_tiles, t;
+  bool fa;
+  __device__ __forceinline__ void init(const PrefillParams& p, int qt, int q_end, bool is_fa) {
+    fa = is_fa;
+    t = qt;
+    col_idx = p.col_idx;
+    rp0 = 0;
+    if (fa) {
+      n_tiles = (q_end + BN - 1) / BN;
+    } else {
+      const int mrow = min(qt, p.mask_blocks - 1);
+      rp0 = p.row_ptr[mrow];
+      n_tiles = max(p.row_ptr[mrow + 1] - rp0, 0) * TPB;
+      while (n_tiles > 0 && start(n_tiles - 1) >= q_end) --n_tiles;
+    }
+  }
+  __device__ __forceinline__ int start(int n) const {
+    if (fa) return n * BN;
+    const int blk = min(max(col_idx[rp0 + n / TPB], 0), t);
+    return blk * BM + (n % TPB) * BN;
+  }
+  // tiles a wave whose first row is wrow0 must see (up to its last row)
+  __device__ __forceinline__ int visible(int wrow0, int S) const {
+    if (wrow0 >= S) return 0;
+    int n = n_tiles;
+    while (n > 0 && start(n - 1) > wrow0 + 31) --n;
+    return n;
+  }
+};
+
+// Workgroup -> (kv group, query block heaviest first, request, head slot),
+// XCD-major so that consecutive work items share an XCD's L2.
+__device__ __forceinline__ void decode_work(int n_slots, int n_req, int n_qt, int& slot, int& req,
+                                            int& t, int& g) {
+  const int G = gridDim.x, bid = blockIdx.x;
+  int w = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  slot = w % n_slots;
+  w /= n_slots;
+  req = w % n_req;
+  w /= n_req;
+  t = n_qt - 1 - (w % n_qt);
+  g = w / n_qt;
+}
+
+// ---------------------------------------------------------------- single kernel
+template <int D, int BM, int BN, int OCC>
+__global__ __launch_bounds__(BM * 2, OCC) void prefill_single_kernel(const PrefillParams p) {
+  constexpr int NT = BM * 2;
+  using Loader = TileLoader<D, NT, BN>;
+  constexpr int TILEB = Loader::TILEB;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[4 * TILEB];  // K0 K1 V0 V1
+  lds_u8* lds = (lds_u8*)(lds_raw);  // the same array, addressed as LDS
+  lds_u8* kbuf[2] = {lds, lds + TILEB};
+  lds_u8* vbuf[2] = {lds + 2 * TILEB, lds + 3 * TILEB};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
+  const int group = p.hq / p.hkv;
+  const int n_qt = (p.max_seqlen + BM - 1) / BM;
+  int hi, req, t, g;
+  decode_work(group, p.n_req, n_qt, hi, req, t, g);
+  const int head = g * group + hi;
+
+  const int tok0 = p.cu_seqlens[req];
+  const int S = p.cu_seqlens[req + 1] - tok0;
+  const int q0 = t * BM;
+  if (q0 >= S) return;
+  const bool fa = p.route[static_cast<int64_t>(req) * p.n_layers + p.layer] != 0;
+
+  TileList<BM, BN> tiles;
+  tiles.init(p, t, min(q0 + BM, S), fa);
+  Loader ld;
+  ld.init(p.k, p.v, tok0, p.hkv, g, S, tid);
+  WaveAttn<D, BN> wa;
+  wa.init(p.q, tok0, p.hq, head, q0 + wave * 32, S, p.scale, lane);
+  const int n_tiles = tiles.n_tiles;
+  const int n_mine = tiles.visible(q0 + wave * 32, S);
+
+  // Iteration n computes tile n from buffer n%2 while tile n+1 loads.
   if (n_tiles > 0) {
-    const int kst0 = tile_start(0);
-    int kst_nxt = n_tiles > 1 ? tile_start(1) : 0;
-    issue_tile(kbase, kst0, 0);
-    issue_tile(vbase, kst0, 2);
-    if (n_tiles > 1) issue_tile(kbase, kst_nxt, 1);
-    wait_vmem();
+    ld.issue(false, tiles.start(0), kbuf[0]);
+    ld.issue(true, tiles.start(0), vbuf[0]);
+    wait_vmem_all();
     __syncthreads();
-    f32x16 s_cur[2], s_nxt[2];
-    if (n_mine > 0) qk(0, s_cur);
-    int kst_cur = kst0;
     for (int n = 0; n < n_tiles; ++n) {
-      const int kst_n2 = n + 2 < n_tiles ? tile_start(n + 2) : 0;
-      if (n + 2 < n_tiles) issue_tile(kbase, kst_n2, n & 1);
-      if (n + 1 < n_tiles) issue_tile(vbase, kst_nxt, 2 + ((n + 1) & 1));
-      if (n < n_mine) {
-        uint32_t pk[16];
-        if (n + 1 < n_mine) qk((n + 1) & 1, s_nxt);
-        softmax(s_cur, kst_cur, pk);
-        pv(n & 1, pk);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) s_cur[mt] = s_nxt[mt];
+      if (n + 1 < n_tiles) {
+        const int kst = tiles.start(n + 1);
+        ld.issue(false, kst, kbuf[(n + 1) & 1]);
+        ld.issue(true, kst, vbuf[(n + 1) & 1]);
       }
-      wait_vmem();
+      if (n < n_mine) {
+        f32x16 sacc[WaveAttn<D, BN>::MT];
+        uint32_t pk[WaveAttn<D, BN>::PK];
+        wa.qk(kbuf[n & 1], sacc);
+        wa.softmax(sacc, tiles.start(n), pk);
+        wa.pv(vbuf[n & 1], pk);
+      }
+      wait_vmem_all();
       __syncthreads();
-      kst_cur = kst_nxt;
-      kst_nxt = kst_n2;
     }
   }
-
-  // ---- epilogue: O = O^T / l, one query row per lane, 4 consecutive d per store
-  const float lt = l_run + xor32(l_run);
-  if (row_ok) {
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    uint16_t* op = p.out + (static_cast<size_t>(tok0 + row) * p.hq + head) * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = dt * 32 + j * 8 + half * 4;
-        const uint32_t lo = pack_bf16x2(oacc[dt][j * 4] * inv, oacc[dt][j * 4 + 1] * inv);
-        const uint32_t hi2 = pack_bf16x2(oacc[dt][j * 4 + 2] * inv, oacc[dt][j * 4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + d0) = u32x2{lo, hi2};
-      }
-  }
+  wa.store(p.out, tok0, p.hq, head, S);
 }
 
 template <int D, int BM>
 hipError_t launch_typed(const PrefillParams& p, hipStream_t s) {
   const int n_qt = (p.max_seqlen + BM - 1) / BM;
+  const int group = p.hq / p.hkv;
+  (void)group;
   const int64_t grid = static_cast<int64_t>(n_qt) * p.hq * p.n_req;
-  prefill_kernel<D, BM><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
+  prefill_single_kernel<D, BM, kBN, kOcc><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
   return hipGetLastError();
 }
 
