@@ -110,9 +110,13 @@ def main():
         if code != 0:
             raise RuntimeError(f"{what} failed: {flux.status_str(code)}")
 
+    route_ws = torch.empty(flux.route_workspace_size(1, wl.hidden_dim, wl.router_h1), dtype=torch.uint8,
+                           device=dev)
+
     def route_call():
         check(F.flux_route(P(hidden), L.FLUX_BF16, P(cu), 1, wl.hidden_dim, P(w1), P(b1), wl.router_h1,
-                           P(w2), P(b2), wl.n_layers, P(route), None, cstream), "flux_route")
+                           P(w2), P(b2), wl.n_layers, P(route), None, P(route_ws), route_ws.numel(),
+                           cstream), "flux_route")
 
     def mask_call():
         check(F.flux_build_block_mask(S, sa.c(), None, P(row_ptr), P(col_idx), cstream), "mask")

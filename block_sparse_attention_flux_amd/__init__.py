@@ -23,7 +23,7 @@ from . import _lib
 _LIB = _lib.load()
 
 __all__ = [
-    "SAParams", "FluxError", "route", "mask_blocks", "mask_nnz", "build_block_mask",
+    "SAParams", "FluxError", "route", "route_workspace_size", "mask_blocks", "mask_nnz", "build_block_mask",
     "attn_prefill", "decode_workspace_size", "attn_decode", "status_str",
 ]
 
@@ -76,7 +76,11 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def route(hidden, cu_seqlens, w1, b1, w2, b2, route_out=None, logits_out=None):
+def route_workspace_size(n_req, d_in, h1):
+    return int(_LIB.flux_route_workspace_size(n_req, d_in, h1))
+
+
+def route(hidden, cu_seqlens, w1, b1, w2, b2, route_out=None, logits_out=None, workspace=None):
     """Layer Router (flux_route): returns (route uint8 [n_req][L], logits fp32 or None)."""
     if hidden.dtype == torch.bfloat16:
         dt = _lib.FLUX_BF16
@@ -89,11 +93,15 @@ def route(hidden, cu_seqlens, w1, b1, w2, b2, route_out=None, logits_out=None):
     n_layers = w2.shape[0]
     if route_out is None:
         route_out = torch.empty((n_req, n_layers), dtype=torch.uint8, device=hidden.device)
+    if workspace is None:
+        workspace = torch.empty(max(route_workspace_size(n_req, d_in, h1), 1), dtype=torch.uint8,
+                                device=hidden.device)
     code = _LIB.flux_route(
         _ptr(hidden, None, "hidden"), dt, _ptr(cu_seqlens, torch.int32, "cu_seqlens"), n_req, d_in,
         _ptr(w1, torch.float32, "w1"), _ptr(b1, torch.float32, "b1"), h1,
         _ptr(w2, torch.float32, "w2"), _ptr(b2, torch.float32, "b2"), n_layers,
         _ptr(route_out, torch.uint8, "route_out"), _ptr(logits_out, torch.float32, "logits_out"),
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(hidden.device))
     _check(code, "flux_route")
     return route_out, logits_out

@@ -30,7 +30,8 @@ _F = ctypes.c_float
 _S = ctypes.c_size_t
 SIGNATURES = [
     ("flux_status_str", ctypes.c_char_p, [_I]),
-    ("flux_route", _I, [_P, _I, _P, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P]),
+    ("flux_route_workspace_size", _S, [_I, _I, _I]),
+    ("flux_route", _I, [_P, _I, _P, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _S, _P]),
     ("flux_mask_blocks", ctypes.c_int64, [_I, SAParamsC]),
     ("flux_mask_nnz", ctypes.c_int64, [_I, SAParamsC]),
     ("flux_build_block_mask", _I, [_I, SAParamsC, _P, _P, _P, _P]),

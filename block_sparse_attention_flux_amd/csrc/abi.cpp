@@ -59,19 +59,26 @@ const char* flux_status_str(int32_t status) {
   }
 }
 
+size_t flux_route_workspace_size(int32_t n_req, int32_t d_in, int32_t h1) {
+  if (n_req < 1 || d_in < 1 || h1 < 1) return 0;
+  return flux::route_workspace_bytes(n_req, d_in, h1);
+}
+
 flux_status flux_route(const void* hidden, int32_t hidden_dtype, const int32_t* cu_seqlens,
                        int32_t n_req, int32_t d_in, const float* w1, const float* b1, int32_t h1,
                        const float* w2, const float* b2, int32_t n_layers, uint8_t* route_out,
-                       float* logits_out, void* stream) {
+                       float* logits_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (hidden == nullptr || cu_seqlens == nullptr || w1 == nullptr || b1 == nullptr ||
       w2 == nullptr || b2 == nullptr || route_out == nullptr)
     return FLUX_ERR_INVALID_ARG;
   if (hidden_dtype != FLUX_F32 && hidden_dtype != FLUX_BF16) return FLUX_ERR_INVALID_ARG;
   if (n_req < 1 || d_in < 1 || h1 < 1 || n_layers < 1) return FLUX_ERR_INVALID_ARG;
-  if (d_in > 8192 || h1 > 4096 || n_layers > 4096) return FLUX_ERR_UNSUPPORTED;
-  if (n_req > INT32_MAX / 2) return FLUX_ERR_INVALID_ARG;
+  if (d_in > 65536 || h1 > 65536 || n_layers > 65536) return FLUX_ERR_UNSUPPORTED;
+  if (n_req > 65535) return FLUX_ERR_UNSUPPORTED;  // grid y dimension
+  if (workspace == nullptr || workspace_bytes < flux::route_workspace_bytes(n_req, d_in, h1))
+    return FLUX_ERR_WORKSPACE;
   return from_hip(flux::launch_route(hidden, hidden_dtype == FLUX_BF16, cu_seqlens, n_req, d_in,
-                                     w1, b1, h1, w2, b2, n_layers, route_out, logits_out,
+                                     w1, b1, h1, w2, b2, n_layers, route_out, logits_out, workspace,
                                      static_cast<hipStream_t>(stream)));
 }
 

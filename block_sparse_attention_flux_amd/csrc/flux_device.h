@@ -17,6 +17,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
+// Reinterpret 32 bits as fp32.  Takes the value, not a vector element: a
+// __builtin_bit_cast applied directly to an ext_vector element lvalue reads
+// element 0 with this compiler, whatever the index.
+__device__ __forceinline__ float u32_as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+
 // bf16 bits -> fp32 (exact).
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);

@@ -40,10 +40,12 @@ struct DecodeParams {
 hipError_t launch_build_mask(int32_t nb, int32_t sink, int32_t local, uint8_t* mask,
                              int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
 
+// Workspace of the router: pooled vectors then hidden layers, fp32.
+size_t route_workspace_bytes(int32_t n_req, int32_t d_in, int32_t h1);
 hipError_t launch_route(const void* hidden, int32_t bf16, const int32_t* cu, int32_t n_req,
                         int32_t d_in, const float* w1, const float* b1, int32_t h1,
                         const float* w2, const float* b2, int32_t n_layers, uint8_t* route,
-                        float* logits, hipStream_t s);
+                        float* logits, void* workspace, hipStream_t s);
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 

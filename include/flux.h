@@ -79,13 +79,17 @@ const char* flux_status_str(int32_t status);
  * w2, b2      [device] fp32 [n_layers][h1], [n_layers]
  * route_out   [device] uint8 [n_req][n_layers]
  * logits_out  [device] fp32 [n_req][n_layers] or NULL
- * Limits: 1 <= n_req, 1 <= d_in <= 8192, 1 <= h1 <= 4096, 1 <= n_layers <= 4096.
+ * workspace   [device] >= flux_route_workspace_size(n_req, d_in, h1) bytes,
+ *             any contents (holds the pooled vectors and hidden layers).
+ * Limits: 1 <= n_req <= 65535, 1 <= d_in, h1, n_layers <= 65536.
  */
+size_t flux_route_workspace_size(int32_t n_req, int32_t d_in, int32_t h1);
 flux_status flux_route(const void* hidden, int32_t hidden_dtype,
                        const int32_t* cu_seqlens, int32_t n_req, int32_t d_in,
                        const float* w1, const float* b1, int32_t h1,
                        const float* w2, const float* b2, int32_t n_layers,
-                       uint8_t* route_out, float* logits_out, void* stream);
+                       uint8_t* route_out, float* logits_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Number of mask blocks for a sequence: ceil(seqlen / block_size) [host].
  * Returns a negative flux_status on invalid input. */

@@ -28,7 +28,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol():
     syms = declared_symbols()
-    assert len(syms) == 8, syms
+    assert len(syms) == 9, syms
     raw = ctypes.CDLL(LIB)
     for s in syms:
         assert hasattr(raw, s), s
@@ -63,20 +63,26 @@ def test_mask_host_validation():
 
 
 def test_route_validation():
+    ws = lib.flux_route_workspace_size(1, 256, 64)
+    assert ws == 1 * (256 + 64) * 4
+    assert lib.flux_route_workspace_size(0, 256, 64) == 0
     args = dict(hidden=FAKE, dt=0, cu=FAKE, n_req=1, d_in=256, w1=FAKE, b1=FAKE, h1=64, w2=FAKE,
-                b2=FAKE, L=2, route=FAKE, logits=NULL, stream=NULL)
+                b2=FAKE, L=2, route=FAKE, logits=NULL, ws=FAKE, wsb=ws, stream=NULL)
 
     def call(**kw):
         a = dict(args, **kw)
         return lib.flux_route(a["hidden"], a["dt"], a["cu"], a["n_req"], a["d_in"], a["w1"], a["b1"],
-                              a["h1"], a["w2"], a["b2"], a["L"], a["route"], a["logits"], a["stream"])
+                              a["h1"], a["w2"], a["b2"], a["L"], a["route"], a["logits"], a["ws"],
+                              a["wsb"], a["stream"])
     assert call(hidden=NULL) == _lib.FLUX_ERR_INVALID_ARG
     assert call(route=NULL) == _lib.FLUX_ERR_INVALID_ARG
     assert call(dt=5) == _lib.FLUX_ERR_INVALID_ARG
     assert call(n_req=0) == _lib.FLUX_ERR_INVALID_ARG
     assert call(L=0) == _lib.FLUX_ERR_INVALID_ARG
-    assert call(d_in=8193) == _lib.FLUX_ERR_UNSUPPORTED
-    assert call(h1=5000) == _lib.FLUX_ERR_UNSUPPORTED
+    assert call(d_in=65537) == _lib.FLUX_ERR_UNSUPPORTED
+    assert call(n_req=70000) == _lib.FLUX_ERR_UNSUPPORTED
+    assert call(ws=NULL) == _lib.FLUX_ERR_WORKSPACE
+    assert call(wsb=ws - 1) == _lib.FLUX_ERR_WORKSPACE
 
 
 PREFILL_OK = dict(q=FAKE, k=FAKE, v=ctypes.c_void_p(0x2000), out=ctypes.c_void_p(0x3000), cu=FAKE,

@@ -68,7 +68,8 @@ def check_route(route_gpu, z_gpu, route_ref, z_ref, w2, h_bound):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_router_tiny_and_varlen(dtype):
     say(f"router dtype={dtype}")
-    cases = [((512,), 256, 64, 2), ((150, 200, 201, 3000, 1, 777, 99, 4096), 4096, 256, 32)]
+    cases = [((512,), 256, 64, 2), ((150, 200, 201, 3000, 1, 777, 99, 4096), 4096, 256, 32),
+             ((131072, 333), 264, 256, 36)]
     for lens, D, H1, L in cases:
         g = syn.generator(7 + D, DEV)
         T = sum(lens)
