@@ -259,7 +259,7 @@ def run_decode(args, flux, syn, dev, stream, log):
     route = route_vec[None].repeat(n_seq, 1).to(dev).contiguous()
     seqlens = torch.full((n_seq,), ctx, dtype=torch.int32, device=dev)
     _, rp, ci = flux.build_block_mask(ctx, sa, device=dev, dense=False)
-    ws = torch.empty(flux.decode_workspace_size(n_seq, hq, hkv, d, ctx), dtype=torch.uint8, device=dev)
+    ws = flux.decode_workspace(n_seq, hq, hkv, d, ctx, dev)
 
     def step(timers=None):
         for layer in range(nl):

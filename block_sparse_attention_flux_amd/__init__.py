@@ -24,7 +24,7 @@ _LIB = _lib.load()
 
 __all__ = [
     "SAParams", "FluxError", "route", "route_workspace_size", "mask_blocks", "mask_nnz", "build_block_mask",
-    "attn_prefill", "decode_workspace_size", "attn_decode", "status_str",
+    "attn_prefill", "decode_workspace_size", "decode_workspace", "attn_decode", "status_str",
 ]
 
 
@@ -161,6 +161,12 @@ def decode_workspace_size(n_seq, hq, hkv, head_dim, max_len):
     return int(_LIB.flux_attn_decode_workspace_size(n_seq, hq, hkv, head_dim, max_len))
 
 
+def decode_workspace(n_seq, hq, hkv, head_dim, max_len, device="cuda"):
+    """A device buffer of flux_attn_decode_workspace_size bytes (zero-filled)."""
+    return torch.zeros(max(decode_workspace_size(n_seq, hq, hkv, head_dim, max_len), 1),
+                       dtype=torch.uint8, device=device)
+
+
 def attn_decode(q, k_cache, v_cache, seqlens, route, layer, row_ptr, col_idx, sa,
                 workspace=None, out=None, softmax_scale=None):
     """One split-KV decode step of one layer (flux_attn_decode)."""
@@ -173,8 +179,7 @@ def attn_decode(q, k_cache, v_cache, seqlens, route, layer, row_ptr, col_idx, sa
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        ws_bytes = decode_workspace_size(n_seq, hq, hkv, d, max_len)
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(n_seq, hq, hkv, d, max_len, q.device)
     code = _LIB.flux_attn_decode(
         _ptr(q, torch.bfloat16, "q"), _ptr(k_cache, torch.bfloat16, "k_cache"),
         _ptr(v_cache, torch.bfloat16, "v_cache"), _ptr(out, torch.bfloat16, "out"),

@@ -267,6 +267,27 @@ def test_decode_32k_sampled():
         assert_attn_close(f32(out)[seqs], ref, f"decode32k layer {layer}")
 
 
+def test_decode_workspace_reuse():
+    """One workspace, sized for the largest call, serves calls of different
+    shapes one after another; results equal those of a fresh workspace."""
+    say("decode workspace reuse")
+    big = (4, 6000, [6000, 4097, 1, 5000], 32, 8, 128)
+    small = (2, 3000, [3000, 1500], 16, 4, 64)
+    ws = flux.decode_workspace(4, 32, 8, 128, 6000, DEV)
+    for case in (big, small, big):
+        n_seq, max_len, seqlens, hq, hkv, d = case
+        q, kc, vc, sl = make_decode(n_seq, max_len, seqlens, hq, hkv, d, 91 + d)
+        sa = flux.SAParams(128, 1, 4)
+        _, rp, ci = flux.build_block_mask(max_len, sa, dense=False)
+        route = torch.tensor([[1, 0]] * n_seq, dtype=torch.uint8, device=DEV)
+        for layer in (0, 1):
+            assert flux.decode_workspace_size(n_seq, hq, hkv, d, max_len) <= ws.numel()
+            shared = flux.attn_decode(q, kc, vc, sl, route, layer, rp, ci, sa, workspace=ws)
+            fresh = flux.attn_decode(q, kc, vc, sl, route, layer, rp, ci, sa)
+            torch.cuda.synchronize()
+            assert torch.equal(shared, fresh)
+
+
 def test_decode_matches_prefill_last_row():
     say("decode vs prefill last row")
     S, hq, hkv, d = 1500, 8, 2, 128
