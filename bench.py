@@ -254,7 +254,7 @@ def run_decode(args, flux, syn, dev, stream, log):
     kc = [syn.normal((n_seq, hkv, ctx, d), g, dev) for _ in range(nl)]
     vc = [syn.normal((n_seq, hkv, ctx, d), g, dev) for _ in range(nl)]
     q = [syn.normal((n_seq, hq, d), g, dev) for _ in range(nl)]
-    out = torch.empty((n_seq, hq, d), dtype=torch.bfloat16, device=dev)
+    out = [torch.empty((n_seq, hq, d), dtype=torch.bfloat16, device=dev) for _ in range(nl)]
     route_vec = syn.seeded_route(nl, wl.n_sa_layers, wl.seed)
     route = route_vec[None].repeat(n_seq, 1).to(dev).contiguous()
     seqlens = torch.full((n_seq,), ctx, dtype=torch.int32, device=dev)
@@ -267,7 +267,8 @@ def run_decode(args, flux, syn, dev, stream, log):
                 e = torch.cuda.Event(enable_timing=True)
                 e.record(stream)
                 timers.append(e)
-            flux.attn_decode(q[layer], kc[layer], vc[layer], seqlens, route, layer, rp, ci, sa, ws, out)
+            flux.attn_decode(q[layer], kc[layer], vc[layer], seqlens, route, layer, rp, ci, sa, ws,
+                             out[layer])
         if timers is not None:
             e = torch.cuda.Event(enable_timing=True)
             e.record(stream)
@@ -287,6 +288,29 @@ def run_decode(args, flux, syn, dev, stream, log):
         lay += np.array([tm[i].elapsed_time(tm[i + 1]) for i in range(nl)])
     lay /= args.decode_steps
     step_ms = float(np.mean(per_step))
+
+    # The same step captured once in a HIP graph and replayed: the host's
+    # launch gaps between the 72 kernels disappear.  Every checked replay must
+    # reproduce the eager outputs bit for bit.
+    eager = [o.clone() for o in out]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(2):
+        for o in out:
+            o.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(out, eager)):
+            raise RuntimeError("decode graph replay differs from the eager step")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.decode_steps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / args.decode_steps
+    del graph
     fa_layers = [i for i in range(nl) if int(route_vec[i]) == 1]
     sa_layers = [i for i in range(nl) if int(route_vec[i]) == 0]
     sa_keys = (wl.sink_blocks + wl.local_blocks) * wl.block_size
@@ -298,12 +322,16 @@ def run_decode(args, flux, syn, dev, stream, log):
     sa_ms = float(lay[sa_layers].mean())
     gbs = step_bytes / (step_ms * 1e-3) / 1e9
     fa_gbs = fa_bytes / (fa_ms * 1e-3) / 1e9
-    log(f"decode step {step_ms:.3f} ms ({16 / step_ms * 1e3:.0f} tok/s)  FA layer {fa_ms:.3f} ms "
-        f"({fa_gbs:.0f} GB/s)  SA layer {sa_ms:.3f} ms ({sa_bytes / sa_ms / 1e6:.0f} GB/s)")
+    log(f"decode step {step_ms:.3f} ms ({16 / step_ms * 1e3:.0f} tok/s), graph replay {graph_ms:.3f} ms  "
+        f"FA layer {fa_ms:.3f} ms ({fa_gbs:.0f} GB/s)  SA layer {sa_ms:.3f} ms "
+        f"({sa_bytes / sa_ms / 1e6:.0f} GB/s)")
     res = {
         "workload": "Qwen3-4B-shaped decode, 16 seqs x 32768 ctx, 36 layers (18 FA / 18 SA seeded)",
         "value": round(n_seq / (step_ms * 1e-3), 1), "unit": "tok/s",
         "ms_per_step": round(step_ms, 4), "steps": args.decode_steps,
+        "graph_ms_per_step": round(graph_ms, 4),
+        "graph_tok_s": round(n_seq / (graph_ms * 1e-3), 1),
+        "graph_gbs": round(step_bytes / (graph_ms * 1e-3) / 1e9, 1),
         "fa_layer_ms": round(fa_ms, 4), "sa_layer_ms": round(sa_ms, 4),
         "bytes_per_step": step_bytes,
         "roofline": {"kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",

@@ -48,4 +48,30 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Value of lane (lane ^ 32), through the LDS crossbar (no LDS memory).
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
 
+// Both 32-lane halves of v after v_permlane32_swap: lo[l] = v[l % 32],
+// hi[l] = v[l % 32 + 32] (one VALU op, no LDS).
+__device__ __forceinline__ void halves(float v, float& lo, float& hi) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  lo = u32_as_f32(r[0]);
+  hi = u32_as_f32(r[1]);
+}
+// max / sum of lanes l and l ^ 32, the same value (and bits) in both lanes
+__device__ __forceinline__ float max_halves(float v) {
+  float lo, hi;
+  halves(v, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  float lo, hi;
+  halves(v, lo, hi);
+  return lo + hi;
+}
+
+// a.x + a.y + c for a packed bf16 pair a (v_dot2c_f32_bf16 against (1, 1))
+__device__ __forceinline__ float add_bf16_pair(uint32_t a, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), c, false);
+}
+
 }  // namespace flux

@@ -234,7 +234,7 @@ struct WaveAttn {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_halves(mx);
     const float mxs = mx * cs;
     // Rows whose max grew past the slack move their max; every other row keeps
     // it and scales by exactly 1.  The multiply is skipped when no row moved.
@@ -248,17 +248,22 @@ struct WaveAttn {
       m_run = m_new;
     }
     const float mu = (m_run == kNegInf) ? 0.0f : m_run;
-    float psum = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(__builtin_fmaf(sacc[mt][r], cs, -mu));
         const float p1 = fast_exp2(__builtin_fmaf(sacc[mt][r + 1], cs, -mu));
-        psum += p0 + p1;
         pk[mt * 8 + r / 2] = pack_bf16x2(p0, p1);
       }
-    l_run += psum;
+    // the row sum takes the bf16 P that the P V product uses, two pairs per op
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PK; i += 2) {
+      s0 = add_bf16_pair(pk[i], s0);
+      s1 = add_bf16_pair(pk[i + 1], s1);
+    }
+    l_run += s0 + s1;
   }
 
   __device__ __forceinline__ s16x4 vt_read(const lds_u8* vl, int blk) const {
@@ -291,7 +296,7 @@ struct WaveAttn {
 
   // O = O^T / l, one query row per lane, 4 consecutive d per store
   __device__ __forceinline__ void store(uint16_t* out, int tok0, int hq, int head, int S) const {
-    const float lt = l_run + xor32(l_run);
+    const float lt = sum_halves(l_run);
     if (row < S) {
       const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
       uint16_t* op = out + (static_cast<size_t>(tok0 + row) * hq + head) * D;
@@ -364,10 +369,17 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_single_kernel(const Prefi
   constexpr int NT = BM * 2;
   using Loader = TileLoader<D, NT, BN>;
   constexpr int TILEB = Loader::TILEB;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[4 * TILEB];  // K0 K1 V0 V1
-  lds_u8* lds = (lds_u8*)(lds_raw);  // the same array, addressed as LDS
-  lds_u8* kbuf[2] = {lds, lds + TILEB};
-  lds_u8* vbuf[2] = {lds + 2 * TILEB, lds + 3 * TILEB};
+  // Four separate arrays: the compiler can then see that the LDS reads of
+  // one buffer pair never alias the DMA still filling the other pair, and
+  // does not make the reads wait for it.
+  __shared__ __attribute__((aligned(16))) unsigned char k0_raw[TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char k1_raw[TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char v0_raw[TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char v1_raw[TILEB];
+  lds_u8* const k0 = (lds_u8*)(k0_raw);  // the same arrays, addressed as LDS
+  lds_u8* const k1 = (lds_u8*)(k1_raw);
+  lds_u8* const v0 = (lds_u8*)(v0_raw);
+  lds_u8* const v1 = (lds_u8*)(v1_raw);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
@@ -392,27 +404,39 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_single_kernel(const Prefi
   const int n_tiles = tiles.n_tiles;
   const int n_mine = tiles.visible(q0 + wave * 32, S);
 
-  // Iteration n computes tile n from buffer n%2 while tile n+1 loads.
-  if (n_tiles > 0) {
-    ld.issue(false, tiles.start(0), kbuf[0]);
-    ld.issue(true, tiles.start(0), vbuf[0]);
+  // Step n computes tile n from one buffer pair while tile n+1 loads into the
+  // other; the loop is unrolled by two so that each step names its buffers.
+  // kst is the first key of tile n (looked up one step ahead, so no index
+  // load waits behind the tile loads in flight).
+  int kst = 0;
+  auto step = [&](int n, const lds_u8* kc, const lds_u8* vc, lds_u8* kn, lds_u8* vn) {
+    int kst_next = 0;
+    if (n + 1 < n_tiles) {
+      kst_next = tiles.start(n + 1);
+      ld.issue(false, kst_next, kn);
+      ld.issue(true, kst_next, vn);
+    }
+    if (n < n_mine) {
+      f32x16 sacc[WaveAttn<D, BN>::MT];
+      uint32_t pk[WaveAttn<D, BN>::PK];
+      wa.qk(kc, sacc);
+      wa.softmax(sacc, kst, pk);
+      wa.pv(vc, pk);
+    }
+    kst = kst_next;
     wait_vmem_all();
     __syncthreads();
-    for (int n = 0; n < n_tiles; ++n) {
-      if (n + 1 < n_tiles) {
-        const int kst = tiles.start(n + 1);
-        ld.issue(false, kst, kbuf[(n + 1) & 1]);
-        ld.issue(true, kst, vbuf[(n + 1) & 1]);
-      }
-      if (n < n_mine) {
-        f32x16 sacc[WaveAttn<D, BN>::MT];
-        uint32_t pk[WaveAttn<D, BN>::PK];
-        wa.qk(kbuf[n & 1], sacc);
-        wa.softmax(sacc, tiles.start(n), pk);
-        wa.pv(vbuf[n & 1], pk);
-      }
-      wait_vmem_all();
-      __syncthreads();
+  };
+  if (n_tiles > 0) {
+    kst = tiles.start(0);
+    ld.issue(false, kst, k0);
+    ld.issue(true, kst, v0);
+    wait_vmem_all();
+    __syncthreads();
+    for (int n = 0; n < n_tiles; n += 2) {
+      step(n, k0, v0, k1, v1);
+      if (n + 1 >= n_tiles) break;
+      step(n + 1, k1, v1, k0, v0);
     }
   }
   wa.store(p.out, tok0, p.hq, head, S);
