@@ -122,6 +122,8 @@ flux_status flux_attn_prefill(const uint16_t* q, const uint16_t* k, const uint16
   if (st != FLUX_OK) return st;
   const int64_t n_qt = (static_cast<int64_t>(max_seqlen) + p.block_size - 1) / p.block_size;
   if (n_qt * hq * n_req > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
+  // K/V rows of one request are addressed with 32-bit byte offsets
+  if (static_cast<int64_t>(max_seqlen) * hkv * head_dim * 2 > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
   flux::PrefillParams pp{};
   pp.q = q; pp.k = k; pp.v = v; pp.out = out;
   pp.cu_seqlens = cu_seqlens; pp.route = route;

@@ -56,6 +56,9 @@ namespace {
 constexpr int kBN = 32;                // keys per tile
 constexpr int kOcc = 3;                // waves per SIMD the kernel is built for
 constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag
+// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
+// no swizzle, no index stride (byte-addressed, range-checked per lane).
+constexpr int kBufferFlags = 0x00020000;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -132,27 +135,22 @@ struct TileLoader {
       voff[j] = r * row_bytes + c * 16;
     }
   }
-  // Issue the loads of the tile starting at key kst into LDS at `dst`.
+  // Issue the loads of the tile starting at key kst into LDS at `dst`.  The
+  // tile is read through a buffer resource whose range ends at the last key
+  // of the sequence: rows at or past S come back as zeros from the hardware
+  // range check, so a ragged last tile needs no separate path (its keys are
+  // masked as causal, and zero V rows add nothing).
   __device__ __forceinline__ void issue(bool is_v, int kst, lds_u8* dst) const {
-    const unsigned char* base = is_v ? vbase : kbase;
+    const unsigned char* base = (is_v ? vbase : kbase) + static_cast<size_t>(kst) * row_bytes;
+    const uint32_t rows = static_cast<uint32_t>(min(S - kst, BN));
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(base), 0, static_cast<int>(rows * row_bytes), kBufferFlags);
     lds_u8* dst0 = dst + wave_u * 64 * 16;
-    if (kst + BN <= S) {
-      const unsigned char* sb = base + static_cast<size_t>(kst) * row_bytes;  // uniform
 #pragma unroll
-      for (int j = 0; j < LOADS; ++j)
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(sb + (is_v ? voff[j] : koff[j])),
-                                         reinterpret_cast<lds_void*>(dst0 + j * NT * 16), 16, 0, 0);
-    } else {  // last tile of the sequence: rows past the end read the last row (masked later)
-#pragma unroll
-      for (int j = 0; j < LOADS; ++j) {
-        int r, c;
-        if (is_v) v_src(j, r, c); else k_src(j, r, c);
-        const int key = min(kst + r, S - 1);
-        __builtin_amdgcn_global_load_lds(
-            static_cast<const void*>(base + static_cast<size_t>(key) * row_bytes + c * 16),
-            reinterpret_cast<lds_void*>(dst0 + j * NT * 16), 16, 0, 0);
-      }
-    }
+    for (int j = 0; j < LOADS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, reinterpret_cast<lds_void*>(dst0 + j * NT * 16),
+                                               16, static_cast<int>(is_v ? voff[j] : koff[j]), 0, 0,
+                                               0);
   }
 };
 
