@@ -202,12 +202,17 @@ def main():
             "fa_tok_s": round(S / (fa_ms * 1e-3), 1), "sa_tok_s": round(S / (sa_ms * 1e-3), 1),
         },
         "roofline": {
-            "kernel": "prefill_kernel<128,128> (FA + SA launches)",
+            "kernel": "prefill_kernel<128,128,32,3> (FA + SA launches)",
             "bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": None,
         },
     }
+    att = attainable(flux, dev, stream, log)
+    result["attainable"] = att
+    result["roofline"]["frac_attainable"] = round(pre_tflops / att["mfma_tflops"], 4)
+    result["prefill"]["fa_frac_attainable"] = round(fa_flops / fa_ms / 1e9 / att["mfma_tflops"], 4)
+    result["prefill"]["sa_frac_attainable"] = round(sa_flops / sa_ms / 1e9 / att["mfma_tflops"], 4)
     tr = counted_traffic("prefill_kernel")
     if tr is not None:
         result["roofline"]["traffic"] = round(tr["per_launch_bytes"])
@@ -219,6 +224,8 @@ def main():
     # ------------------------------------------------------------ decode phase
     if not args.no_decode:
         result["decode"] = run_decode(args, flux, syn, dev, stream, log)
+        result["decode"]["roofline"]["frac_attainable"] = round(
+            result["decode"]["roofline"]["achieved"] / att["hbm_read_gbs"], 4)
 
     # ------------------------------------------------------------ oracle on the host
     if not args.no_cpu_baseline:
@@ -226,6 +233,37 @@ def main():
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def attainable(flux, dev, stream, log):
+    """What this GPU reaches on a dense bf16 MFMA loop and on a streaming HBM
+    read (the library's probe kernels): the ceilings beside the published peaks."""
+    import torch
+
+    def best_ms(fn, reps=3):
+        fn()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return min(out)
+
+    n_wg, iters = 256 * 3, 4096  # 12 waves per CU, as the prefill kernel runs
+    sink = torch.empty(n_wg, dtype=torch.float32, device=dev)
+    flops = flux.probe_mfma(sink, n_wg, iters)
+    mfma_tflops = flops / best_ms(lambda: flux.probe_mfma(sink, n_wg, iters)) / 1e9
+    src = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    rsink = torch.empty(4096, dtype=torch.int32, device=dev)
+    read_gbs = src.numel() / best_ms(lambda: flux.probe_read(src, rsink)) / 1e6
+    del src
+    log(f"attainable: bf16 MFMA loop {mfma_tflops:.0f} TF/s, HBM streaming read {read_gbs:.0f} GB/s")
+    return {"mfma_tflops": round(mfma_tflops, 1), "hbm_read_gbs": round(read_gbs, 1),
+            "how": "library probe kernels: 768 workgroups x 4 waves of v_mfma_f32_32x32x16_bf16 chains; "
+                   "one read of a 2 GiB buffer with 16-byte loads; best of 3"}
 
 
 def counted_traffic(kernel):

@@ -25,6 +25,7 @@ _LIB = _lib.load()
 __all__ = [
     "SAParams", "FluxError", "route", "route_workspace_size", "mask_blocks", "mask_nnz", "build_block_mask",
     "attn_prefill", "decode_workspace_size", "decode_workspace", "attn_decode", "status_str",
+    "probe_mfma", "probe_read",
 ]
 
 
@@ -190,3 +191,21 @@ def attn_decode(q, k_cache, v_cache, seqlens, route, layer, row_ptr, col_idx, sa
         workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(code, "flux_attn_decode")
     return out
+
+
+# ---------------------------------------------------------------- measurement probes
+
+
+def probe_mfma(sink, n_workgroups, iters):
+    """Dense bf16 MFMA loop (flux_probe_mfma); returns the launch's flops."""
+    code = _LIB.flux_probe_mfma(_ptr(sink, torch.float32, "sink"), int(n_workgroups), int(iters),
+                                _stream(sink.device))
+    _check(code, "flux_probe_mfma")
+    return float(_LIB.flux_probe_mfma_flops(int(n_workgroups), int(iters)))
+
+
+def probe_read(src, sink):
+    """Streaming read of every byte of src (flux_probe_read); one word per workgroup in sink."""
+    code = _LIB.flux_probe_read(_ptr(src, None, "src"), src.numel() * src.element_size(),
+                                _ptr(sink, torch.int32, "sink"), sink.numel(), _stream(src.device))
+    _check(code, "flux_probe_read")

@@ -1,4 +1,5 @@
-"""ctypes loader and prototypes for libflux.so (declared in include/flux.h).
+"""ctypes loader and prototypes for libflux.so (declared in include/flux.h and
+include/flux_probe.h).
 
 Loading fails loudly: there is no fallback implementation of any entry point.
 """
@@ -41,6 +42,12 @@ SIGNATURES = [
     ("flux_attn_decode", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P, _P, _I,
                               SAParamsC, _P, _S, _P]),
 ]
+# measurement probes (include/flux_probe.h)
+PROBE_SIGNATURES = [
+    ("flux_probe_mfma", _I, [_P, _I, _I, _P]),
+    ("flux_probe_mfma_flops", ctypes.c_double, [_I, _I]),
+    ("flux_probe_read", _I, [_P, _S, _P, _I, _P]),
+]
 
 _lib = None
 
@@ -55,7 +62,7 @@ def load(path=LIB_PATH):
             f"libflux.so not found at {path}; build it first with "
             "`python block_sparse_attention_flux_amd/build.py` (needs hipcc)")
     lib = ctypes.CDLL(path)
-    for name, res, args in SIGNATURES:
+    for name, res, args in SIGNATURES + PROBE_SIGNATURES:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args

@@ -5,40 +5,35 @@
 //
 // Work decomposition
 //   A workgroup owns one query block of BM rows (BM = the mask block size, 64
-//   or 128) of one request.  Each wave owns 32 query rows of one query head.
-//   Key tiles of BN = 64 keys.  FA visits every tile up to the diagonal; SA
-//   visits only the tiles of the blocks listed in the query block's CSR row,
-//   so inactive K/V tiles are never loaded.
+//   or 128) of one query head of one request; each of its BM/32 waves owns 32
+//   query rows.  Keys are visited in tiles of BN = 32: FA visits every tile up
+//   to the diagonal, SA only the tiles of the blocks in the query block's CSR
+//   row, so inactive K/V tiles are never loaded.  A wave skips the tiles
+//   that start past its last row (it still joins the block's barriers).
 //
 // Per key tile and wave (bf16 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulate):
 //   S^T[key][q] = K Q^T      A = K rows from LDS, B = Q kept in registers
-//   online softmax in the log2 domain, row max across the two lane halves
+//   online softmax in the log2 domain; row max and row sum combine the two
+//   lane halves with v_permlane32_swap
 //   O^T[d][q] += V^T P^T     A = V^T via the LDS transpose read, B = P
 //   The transposed products put one query row in each lane (q = lane % 32),
 //   so softmax statistics and the O rescale are per-lane scalars and P lands
-//   directly in the B-operand layout of the second MFMA.  Each product issues
-//   all of its LDS operand reads before its MFMAs so the reads overlap.
+//   directly in the B-operand layout of the second MFMA.  The row sum is
+//   taken over the same bf16 P that the second product uses (v_dot2c).
 //
 // Data movement
-//   K and V tiles go global -> LDS directly (global_load_lds_dwordx4, no
-//   register staging): K row-major with XOR-swizzled 16-byte chunks, V in
-//   128-byte blocks of 4 keys x 16 d; every LDS read below is bank-conflict
-//   free.  V^T operands come from ds_read_b64_tr_b16: within each 16-lane
-//   group, destination lane 4i+j receives element j of source lanes i, i+4,
-//   i+8, i+12, so four source lanes pointing at four keys deliver those keys'
-//   values of one d column.
-//
-// Two kernels
-//   pair kernel (query heads per KV head even, the common GQA case): 2*BM/32
-//     waves = two query heads of the same KV group over the same rows, so
-//     every K/V tile in LDS feeds twice the waves.  The two head groups run
-//     half a tile apart: while one group does K Q^T + softmax (MFMA + VALU),
-//     the other does its P V MFMAs, and they swap at the next barrier, so the
-//     two waves that share a SIMD keep its matrix core and its VALU busy at
-//     the same time.  K and V loads alternate per half step and each gets a
-//     whole tile of latency cover.
-//   single kernel (odd group sizes): BM/32 waves of one head, K/V of the
-//     next tile loaded while the current one is computed.
+//   K and V tiles go global -> LDS directly (buffer_load_dwordx4 ... lds, no
+//   register staging) through a buffer resource whose range ends at the last
+//   key of the sequence, so a ragged last tile reads zeros.  K is row-major
+//   with XOR-swizzled 16-byte chunks, V in 128-byte blocks of 4 keys x 16 d;
+//   every LDS read below is bank-conflict free.  V^T operands come from
+//   ds_read_b64_tr_b16: within each 16-lane group, destination lane 4i+j
+//   receives element j of source lanes i, i+4, i+8, i+12, so four source
+//   lanes pointing at four keys deliver those keys' values of one d column.
+//   Two K and two V buffers live in four separate LDS arrays: tile n is
+//   computed from one pair while tile n+1 loads into the other.  With
+//   separate arrays the compiler can tell that the LDS reads never alias the
+//   DMA in flight and does not make them wait for it.
 //
 // The running max is only moved when a row's max grows by more than 2^8 (the
 // final normalisation divides by a sum taken with the same stale max, so the
@@ -361,9 +356,8 @@ __device__ __forceinline__ void decode_work(int n_slots, int n_req, int n_qt, in
   g = w / n_qt;
 }
 
-// ---------------------------------------------------------------- single kernel
 template <int D, int BM, int BN, int OCC>
-__global__ __launch_bounds__(BM * 2, OCC) void prefill_single_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParams p) {
   constexpr int NT = BM * 2;
   using Loader = TileLoader<D, NT, BN>;
   constexpr int TILEB = Loader::TILEB;
@@ -446,7 +440,7 @@ hipError_t launch_typed(const PrefillParams& p, hipStream_t s) {
   const int group = p.hq / p.hkv;
   (void)group;
   const int64_t grid = static_cast<int64_t>(n_qt) * p.hq * p.n_req;
-  prefill_single_kernel<D, BM, kBN, kOcc><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
+  prefill_kernel<D, BM, kBN, kOcc><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
   return hipGetLastError();
 }
 

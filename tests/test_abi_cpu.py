@@ -21,8 +21,11 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation rejects the cal
 SA = _lib.SAParamsC
 
 
-def declared_symbols():
-    text = open(HEADER).read()
+PROBE_HEADER = HEADER.replace("flux.h", "flux_probe.h")
+
+
+def declared_symbols(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(flux_\w+)\s*\(", text, re.M)))
 
 
@@ -33,6 +36,19 @@ def test_exports_every_declared_symbol():
     for s in syms:
         assert hasattr(raw, s), s
     assert sorted(n for n, _, _ in _lib.SIGNATURES) == syms
+    probes = declared_symbols(PROBE_HEADER)
+    assert len(probes) == 3, probes
+    for s in probes:
+        assert hasattr(raw, s), s
+    assert sorted(n for n, _, _ in _lib.PROBE_SIGNATURES) == probes
+
+
+def test_probe_host_validation():
+    assert lib.flux_probe_mfma(NULL, 4, 4, NULL) == -1
+    assert lib.flux_probe_mfma(FAKE, 0, 4, NULL) == -1
+    assert lib.flux_probe_read(FAKE, 20, FAKE, 4, NULL) == -1  # not a multiple of 16
+    assert lib.flux_probe_read(NULL, 4096, FAKE, 4, NULL) == -1
+    assert lib.flux_probe_mfma_flops(2, 3) == 4 * 2 * 3 * 4 * 32 * 32 * 16 * 2
 
 
 def test_status_strings():
