@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 131072-token routed prefill and the varlen8 prefill + decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
     ap.add_argument("--copy-probe", action="store_true",
@@ -227,6 +229,11 @@ def main():
         result["decode"]["roofline"]["frac_attainable"] = round(
             result["decode"]["roofline"]["achieved"] / att["hbm_read_gbs"], 4)
 
+    # ------------------------------------------------------------ long workloads
+    if not args.no_long:
+        result["prefill131k"] = run_prefill_131k(flux, syn, dev, stream, log)
+        result["varlen8"] = run_varlen8(flux, syn, dev, stream, log)
+
     # ------------------------------------------------------------ oracle on the host
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, q, k, v, S, wl, log)
@@ -277,6 +284,187 @@ def counted_traffic(kernel):
     except (OSError, KeyError, ValueError):
         return None
     return rec if hashlib.sha256(src).hexdigest() == rec["source_sha256"] else None
+
+
+def _events(torch, stream, n):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    return ev
+
+
+def run_prefill_131k(flux, syn, dev, stream, log):
+    """The 131072-token workload: router on 131072 x 2560 bf16 hidden states
+    (2560 -> 256 -> 36), mask, then all 36 layers routed by the router's
+    decisions.  The 36 layers share one q/k/v set (1.5 GiB; every layer has
+    the same shapes and the kernels are compute-bound, so the time is that of
+    36 distinct layers).  One untimed pass, then one timed pass with an event
+    around every layer."""
+    import torch
+
+    wl = syn.PREFILL128K
+    S, L, d = wl.seqlens[0], wl.n_layers, wl.head_dim
+    g = syn.generator(wl.seed, dev)
+    hidden = syn.normal((S, wl.hidden_dim), g, dev)
+    w1, b1, w2, b2 = (t.to(dev) for t in syn.router_weights(wl.hidden_dim, wl.router_h1, L, wl.seed))
+    q = syn.normal((S, wl.hq, d), g, dev)
+    k = syn.normal((S, wl.hkv, d), g, dev)
+    v = syn.normal((S, wl.hkv, d), g, dev)
+    out = torch.empty_like(q)
+    cu = syn.cu_seqlens([S], dev)
+    sa = flux.SAParams(wl.block_size, wl.sink_blocks, wl.local_blocks)
+    nb = flux.mask_blocks(S, sa)
+    nnz = flux.mask_nnz(S, sa)
+    rws = torch.empty(flux.route_workspace_size(1, wl.hidden_dim, wl.router_h1), dtype=torch.uint8,
+                      device=dev)
+    route = torch.empty((1, L), dtype=torch.uint8, device=dev)
+
+    def one_pass(ev=None):
+        if ev:
+            ev[0].record(stream)
+        flux.route(hidden, cu, w1, b1, w2, b2, route_out=route, workspace=rws)
+        _, rp, ci = flux.build_block_mask(S, sa, device=dev, dense=False)
+        if ev:
+            ev[1].record(stream)
+        for layer in range(L):
+            flux.attn_prefill(q, k, v, cu, S, route, layer, rp, ci, sa, out=out)
+            if ev:
+                ev[2 + layer].record(stream)
+
+    log("prefill131k: untimed pass")
+    one_pass()
+    torch.cuda.synchronize()
+    ev = _events(torch, stream, L + 2)
+    one_pass(ev)
+    torch.cuda.synchronize()
+    r = route.cpu().numpy()[0]
+    lay = [ev[1 + i].elapsed_time(ev[2 + i]) for i in range(L)]
+    fa = [t for t, x in zip(lay, r) if x == 1]
+    sa_t = [t for t, x in zip(lay, r) if x == 0]
+    pass_ms = ev[0].elapsed_time(ev[L + 1])
+    blk = 4.0 * wl.block_size ** 2 * d * wl.hq
+    fa_fl, sa_fl = nb * (nb + 1) / 2 * blk, nnz * blk
+    res = {"workload": "Qwen3-4B-shaped routed prefill, 131072 tokens, 36 layers routed by the "
+                       "router (2560->256->36), SA window 4096 (1 sink + 32 blocks of 128)",
+           "n_fa_layers": int(r.sum()), "pass_ms": round(pass_ms, 3),
+           "tok_s": round(S / (pass_ms * 1e-3), 1),
+           "router_mask_ms": round(ev[0].elapsed_time(ev[1]), 4)}
+    if fa:
+        res["fa_layer_ms"] = round(sum(fa) / len(fa), 3)
+        res["fa_tflops"] = round(fa_fl / (sum(fa) / len(fa)) / 1e9, 1)
+    if sa_t:
+        res["sa_layer_ms"] = round(sum(sa_t) / len(sa_t), 3)
+        res["sa_tflops"] = round(sa_fl / (sum(sa_t) / len(sa_t)) / 1e9, 1)
+    log(f"prefill131k: {res['n_fa_layers']} FA layers, pass {pass_ms:.1f} ms ({res['tok_s']:.0f} tok/s), "
+        f"FA {res.get('fa_tflops')} TF/s, SA {res.get('sa_tflops')} TF/s")
+    del hidden, q, k, v, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_varlen8(flux, syn, dev, stream, log):
+    """The varlen workload: 8 prompts (seeded lengths in [8192, 65536]), router
+    4096 -> 256 -> 32 per request, all 32 layers of packed prefill routed per
+    request (one q/k/v set shared by the layers), then 128 decode steps over 32
+    layers whose caches start from the prompts and grow by one seeded K/V row
+    per step (the append is tensor indexing, outside the kernels but inside
+    the timed step)."""
+    import numpy as np
+    import torch
+
+    wl = syn.varlen8()
+    lens, L, d, n = list(wl.seqlens), wl.n_layers, wl.head_dim, len(wl.seqlens)
+    T, max_s = sum(lens), max(lens)
+    max_len = max_s + wl.decode_steps
+    g = syn.generator(wl.seed, dev)
+    hidden = syn.normal((T, wl.hidden_dim), g, dev)
+    w1, b1, w2, b2 = (t.to(dev) for t in syn.router_weights(wl.hidden_dim, wl.router_h1, L, wl.seed))
+    cu = syn.cu_seqlens(lens, dev)
+    sa = flux.SAParams(wl.block_size, wl.sink_blocks, wl.local_blocks)
+    _, rp, ci = flux.build_block_mask(max_len, sa, device=dev, dense=False)
+    route, _ = flux.route(hidden, cu, w1, b1, w2, b2)
+    del hidden
+    q = syn.normal((T, wl.hq, d), g, dev)
+    k = syn.normal((T, wl.hkv, d), g, dev)
+    v = syn.normal((T, wl.hkv, d), g, dev)
+    out = torch.empty_like(q)
+
+    def prefill_pass():
+        for layer in range(L):
+            flux.attn_prefill(q, k, v, cu, max_s, route, layer, rp, ci, sa, out=out)
+
+    prefill_pass()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    prefill_pass()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pre_ms = e0.elapsed_time(e1)
+    r = route.cpu().numpy()
+    blk = 4.0 * wl.block_size ** 2 * d * wl.hq
+    flops = 0.0
+    for i, S in enumerate(lens):
+        nb = -(-S // wl.block_size)
+        nnz = flux.mask_nnz(S, sa)
+        flops += (r[i].sum() * nb * (nb + 1) / 2 + (L - r[i].sum()) * nnz) * blk
+    log(f"varlen8 prefill: {T} tokens x {L} layers in {pre_ms:.1f} ms ({T / pre_ms * 1e3:.0f} tok/s, "
+        f"{flops / pre_ms / 1e9:.0f} TF/s)")
+
+    # decode caches: per layer [n][hkv][max_len][d], prompts' K/V first
+    cu_h = np.cumsum([0] + lens)
+    kc, vc = [], []
+    for _ in range(L):
+        a = torch.empty((n, wl.hkv, max_len, d), dtype=torch.bfloat16, device=dev)
+        b = torch.empty_like(a)
+        for i, (s0, s1) in enumerate(zip(cu_h[:-1], cu_h[1:])):
+            a[i, :, :s1 - s0] = k[s0:s1].transpose(0, 1)
+            b[i, :, :s1 - s0] = v[s0:s1].transpose(0, 1)
+        kc.append(a)
+        vc.append(b)
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    ws = flux.decode_workspace(n, wl.hq, wl.hkv, d, max_len, dev)
+    base = torch.tensor(lens, dtype=torch.int32, device=dev)
+    idx = torch.arange(n, device=dev)
+    knew = syn.normal((wl.decode_steps, L, n, wl.hkv, d), g, dev)
+    vnew = syn.normal((wl.decode_steps, L, n, wl.hkv, d), g, dev)
+    qd = syn.normal((wl.decode_steps, L, n, wl.hq, d), g, dev)
+    dout = torch.empty((n, wl.hq, d), dtype=torch.bfloat16, device=dev)
+    e0.record(stream)
+    for t in range(wl.decode_steps):
+        pos = (base + t).long()
+        seqlens = (base + t + 1).to(torch.int32)
+        for layer in range(L):
+            kc[layer][idx, :, pos] = knew[t, layer]
+            vc[layer][idx, :, pos] = vnew[t, layer]
+            flux.attn_decode(qd[t, layer], kc[layer], vc[layer], seqlens, route, layer, rp, ci, sa, ws,
+                             out=dout)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / wl.decode_steps
+    # bytes per step: every visited K/V row once (FA: the whole cache, SA: sink + window rows)
+    row_b = wl.hkv * d * 2 * 2
+    byts = 0
+    for i, S in enumerate(lens):
+        for layer in range(L):
+            N = S + wl.decode_steps // 2
+            if r[i, layer]:
+                byts += N * row_b
+            else:
+                mrow = (N - 1) // wl.block_size
+                byts += min(mrow + 1, wl.sink_blocks + wl.local_blocks) * wl.block_size * row_b
+    res = {"workload": "Llama-3-8B-shaped varlen mix: 8 prompts (seeded lengths in [8192, 65536]), "
+                       "32 layers routed per request by the router (4096->256->32), then 128 decode steps",
+           "lengths": lens, "fa_layers_per_request": r.sum(axis=1).tolist(),
+           "prefill_ms": round(pre_ms, 3), "prefill_tok_s": round(T / (pre_ms * 1e-3), 1),
+           "prefill_tflops": round(flops / pre_ms / 1e9, 1),
+           "decode_ms_per_step": round(dec_ms, 4), "decode_tok_s": round(n / (dec_ms * 1e-3), 1),
+           "decode_gbs": round(byts / (dec_ms * 1e-3) / 1e9, 1),
+           "decode_note": "step time includes the per-layer K/V row append (tensor indexing); bytes at "
+                          "the mid-point cache length"}
+    log(f"varlen8 decode: {dec_ms:.3f} ms/step ({res['decode_tok_s']:.0f} tok/s, {res['decode_gbs']:.0f} GB/s)")
+    del kc, vc, knew, vnew, qd
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_decode(args, flux, syn, dev, stream, log):
