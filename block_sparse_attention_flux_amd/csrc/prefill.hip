@@ -51,6 +51,7 @@ namespace {
 constexpr int kBN = 32;                // keys per tile
 constexpr int kOcc = 3;                // waves per SIMD the kernel is built for
 constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag
+constexpr float kSumLimit = 65536.0f;  // a lane's tile sum of P above this: retake the max
 // Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
 // no swizzle, no index stride (byte-addressed, range-checked per lane).
 constexpr int kBufferFlags = 0x00020000;
@@ -61,6 +62,7 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
 
 // LDS layouts (64 banks of 4 bytes; a 16-byte read is served 16 lanes per
 // pass, an 8-byte read 32 lanes per pass):
@@ -211,7 +213,36 @@ struct WaveAttn {
     }
   }
 
-  // Causal mask, row max, lazy rescale, exponentials -> packed bf16 P
+  // P = 2^(S cs - mu) as packed bf16 pairs; returns this lane's sum of the
+  // same bf16 P that the P V product uses (two pairs per op).
+  __device__ __forceinline__ float exps(const f32x16 (&sacc)[MT], float mu, uint32_t (&pk)[PK]) const {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(sacc[mt][r], cs, -mu));
+        const float p1 = fast_exp2(__builtin_fmaf(sacc[mt][r + 1], cs, -mu));
+        pk[mt * 8 + r / 2] = pack_bf16x2(p0, p1);
+      }
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PK; i += 2) {
+      s0 = add_bf16_pair(pk[i], s0);
+      s1 = add_bf16_pair(pk[i + 1], s1);
+    }
+    return s0 + s1;
+  }
+
+  // Causal mask, exponentials against the running max, and the max update
+  // only where it is needed.  The exponentials are taken first with the
+  // current running max: as long as no P of this lane exceeds 2^16 (its
+  // partial row sum stays below kSumLimit) the tile is done, and the running
+  // max is left as it is (any P up to 2^16 is exact in fp32/bf16 range terms
+  // and the final division uses the same reference).  Otherwise (and on the
+  // first tile, when there is no reference yet) the tile's row max is taken,
+  // rows whose max grew past the slack move their reference (rescaling their
+  // O and sum), and the exponentials are redone; rows that did not move get
+  // bit-identical P, so each row's result depends on its own data only.
   __device__ __forceinline__ void softmax(f32x16 (&sacc)[MT], int kst, uint32_t (&pk)[PK]) {
     if (kst + BN - 1 > wrow0) {  // tile crosses the diagonal: causal mask
 #pragma unroll
@@ -222,41 +253,31 @@ struct WaveAttn {
           if (key > row) sacc[mt][r] = kNegInf;
         }
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
-    mx = max_halves(mx);
-    const float mxs = mx * cs;
-    // Rows whose max grew past the slack move their max; every other row keeps
-    // it and scales by exactly 1.  The multiply is skipped when no row moved.
-    const bool grow = mxs > m_run + kRescaleSlack;
-    if (__ballot(grow) != 0) {
-      const float m_new = grow ? mxs : m_run;
-      const float alpha = !grow ? 1.0f : (m_run == kNegInf) ? 0.0f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-      m_run = m_new;
+    bool redo = m_run == kNegInf;
+    float ps = 0.0f;
+    if (__ballot(redo) == 0) {
+      ps = exps(sacc, m_run, pk);
+      redo = !(ps <= kSumLimit);
     }
-    const float mu = (m_run == kNegInf) ? 0.0f : m_run;
+    if (__ballot(redo) != 0) {
+      float mx = kNegInf;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(sacc[mt][r], cs, -mu));
-        const float p1 = fast_exp2(__builtin_fmaf(sacc[mt][r + 1], cs, -mu));
-        pk[mt * 8 + r / 2] = pack_bf16x2(p0, p1);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+      const float mxs = max_halves(mx) * cs;
+      const bool grow = mxs > m_run + kRescaleSlack;
+      if (__ballot(grow) != 0) {
+        const float m_new = grow ? mxs : m_run;
+        const float alpha = !grow ? 1.0f : (m_run == kNegInf) ? 0.0f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
       }
-    // the row sum takes the bf16 P that the P V product uses, two pairs per op
-    float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < PK; i += 2) {
-      s0 = add_bf16_pair(pk[i], s0);
-      s1 = add_bf16_pair(pk[i + 1], s1);
+      ps = exps(sacc, m_run == kNegInf ? 0.0f : m_run, pk);
     }
-    l_run += s0 + s1;
+    l_run += ps;
   }
 
   __device__ __forceinline__ s16x4 vt_read(const lds_u8* vl, int blk) const {
@@ -307,30 +328,42 @@ struct WaveAttn {
 };
 
 // Query block's key tiles: FA = every tile up to the diagonal, SA = the
-// tiles of the blocks in the CSR row (columns clamped into [0, t]).
+// tiles of the blocks in the CSR row (columns clamped into [0, t]).  The first
+// kLdsCols columns of the row are staged in LDS once, so finding the next
+// tile's start never waits on a global load.
 template <int BM, int BN>
 struct TileList {
   static constexpr int TPB = BM / BN;  // key tiles per mask block
+  static constexpr int kLdsCols = 64;  // CSR entries staged in LDS
   const int32_t* col_idx;
+  const lds_i32* cols;
   int rp0, n_tiles, t;
   bool fa;
-  __device__ __forceinline__ void init(const PrefillParams& p, int qt, int q_end, bool is_fa) {
+  // Every thread of the workgroup calls this (it contains a barrier on the SA path).
+  __device__ __forceinline__ void init(const PrefillParams& p, int qt, int q_end, bool is_fa,
+                                       lds_i32* lds_cols, int tid, int nthreads) {
     fa = is_fa;
     t = qt;
     col_idx = p.col_idx;
+    cols = lds_cols;
     rp0 = 0;
     if (fa) {
       n_tiles = (q_end + BN - 1) / BN;
     } else {
       const int mrow = min(qt, p.mask_blocks - 1);
       rp0 = p.row_ptr[mrow];
-      n_tiles = max(p.row_ptr[mrow + 1] - rp0, 0) * TPB;
+      const int n_blocks = max(p.row_ptr[mrow + 1] - rp0, 0);
+      for (int i = tid; i < min(n_blocks, kLdsCols); i += nthreads)
+        lds_cols[i] = min(max(col_idx[rp0 + i], 0), t);
+      __syncthreads();
+      n_tiles = n_blocks * TPB;
       while (n_tiles > 0 && start(n_tiles - 1) >= q_end) --n_tiles;
     }
   }
   __device__ __forceinline__ int start(int n) const {
     if (fa) return n * BN;
-    const int blk = min(max(col_idx[rp0 + n / TPB], 0), t);
+    const int bi = n / TPB;
+    const int blk = bi < kLdsCols ? cols[bi] : min(max(col_idx[rp0 + bi], 0), t);
     return blk * BM + (n % TPB) * BN;
   }
   // tiles a wave whose first row is wrow0 must see (up to its last row)
@@ -387,8 +420,9 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   if (q0 >= S) return;
   const bool fa = p.route[static_cast<int64_t>(req) * p.n_layers + p.layer] != 0;
 
+  __shared__ int32_t cols_raw[TileList<BM, BN>::kLdsCols];
   TileList<BM, BN> tiles;
-  tiles.init(p, t, min(q0 + BM, S), fa);
+  tiles.init(p, t, min(q0 + BM, S), fa, (lds_i32*)(cols_raw), tid, NT);
   Loader ld;
   ld.init(p.k, p.v, tok0, p.hkv, g, S, tid);
   WaveAttn<D, BN> wa;
