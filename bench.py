@@ -409,33 +409,28 @@ def run_varlen8(flux, syn, dev, stream, log):
     log(f"varlen8 prefill: {T} tokens x {L} layers in {pre_ms:.1f} ms ({T / pre_ms * 1e3:.0f} tok/s, "
         f"{flops / pre_ms / 1e9:.0f} TF/s)")
 
-    # decode caches: per layer [n][hkv][max_len][d], prompts' K/V first
-    cu_h = np.cumsum([0] + lens)
+    # decode caches: per layer [n][hkv][max_len][d], the prompts' K/V first
+    # (mixed per-request routes in a layer: full caches for every layer)
     kc, vc = [], []
     for _ in range(L):
-        a = torch.empty((n, wl.hkv, max_len, d), dtype=torch.bfloat16, device=dev)
-        b = torch.empty_like(a)
-        for i, (s0, s1) in enumerate(zip(cu_h[:-1], cu_h[1:])):
-            a[i, :, :s1 - s0] = k[s0:s1].transpose(0, 1)
-            b[i, :, :s1 - s0] = v[s0:s1].transpose(0, 1)
+        a, b = flux.kv_cache(n, wl.hkv, d, max_len, sa, device=dev)
+        flux.kv_store_prefill(k, v, cu, max_s, a, b, max_len, sa)
         kc.append(a)
         vc.append(b)
     del q, k, v, out
     torch.cuda.empty_cache()
     ws = flux.decode_workspace(n, wl.hq, wl.hkv, d, max_len, dev)
     base = torch.tensor(lens, dtype=torch.int32, device=dev)
-    idx = torch.arange(n, device=dev)
     knew = syn.normal((wl.decode_steps, L, n, wl.hkv, d), g, dev)
     vnew = syn.normal((wl.decode_steps, L, n, wl.hkv, d), g, dev)
     qd = syn.normal((wl.decode_steps, L, n, wl.hq, d), g, dev)
     dout = torch.empty((n, wl.hq, d), dtype=torch.bfloat16, device=dev)
+    seq_t = [(base + t + 1).to(torch.int32) for t in range(wl.decode_steps)]
     e0.record(stream)
     for t in range(wl.decode_steps):
-        pos = (base + t).long()
-        seqlens = (base + t + 1).to(torch.int32)
+        seqlens = seq_t[t]
         for layer in range(L):
-            kc[layer][idx, :, pos] = knew[t, layer]
-            vc[layer][idx, :, pos] = vnew[t, layer]
+            flux.kv_append(knew[t, layer], vnew[t, layer], seqlens, kc[layer], vc[layer], max_len, sa)
             flux.attn_decode(qd[t, layer], kc[layer], vc[layer], seqlens, route, layer, rp, ci, sa, ws,
                              out=dout)
     e1.record(stream)
@@ -459,7 +454,7 @@ def run_varlen8(flux, syn, dev, stream, log):
            "prefill_tflops": round(flops / pre_ms / 1e9, 1),
            "decode_ms_per_step": round(dec_ms, 4), "decode_tok_s": round(n / (dec_ms * 1e-3), 1),
            "decode_gbs": round(byts / (dec_ms * 1e-3) / 1e9, 1),
-           "decode_note": "step time includes the per-layer K/V row append (tensor indexing); bytes at "
+           "decode_note": "step time includes the per-layer K/V row append (flux_kv_append); bytes at "
                           "the mid-point cache length"}
     log(f"varlen8 decode: {dec_ms:.3f} ms/step ({res['decode_tok_s']:.0f} tok/s, {res['decode_gbs']:.0f} GB/s)")
     del kc, vc, knew, vnew, qd
@@ -537,6 +532,43 @@ def run_decode(args, flux, syn, dev, stream, log):
     torch.cuda.synchronize()
     graph_ms = e0.elapsed_time(e1) / args.decode_steps
     del graph
+
+    # The same step with the SA layers on compact caches (sink rows + a ring
+    # of the window: 2176 rows per head instead of 32768); FA layers unchanged.
+    sa_set = set(i for i in range(nl) if int(route_vec[i]) == 0)
+    cmp_caches = {}
+    for layer in sa_set:
+        kc[layer] = vc[layer] = None  # the full SA caches are not needed any more
+    torch.cuda.empty_cache()
+    for layer in sa_set:
+        shape = (n_seq, hkv, flux.kv_rows(ctx, sa, compact=True), d)
+        cmp_caches[layer] = (syn.normal(shape, g, dev), syn.normal(shape, g, dev))
+    ws2 = flux.decode_workspace(n_seq, hq, hkv, d, ctx, dev)
+
+    def step_compact():
+        for layer in range(nl):
+            if layer in sa_set:
+                a, b = cmp_caches[layer]
+                flux.attn_decode_sa_compact(q[layer], a, b, seqlens, ctx, rp, ci, sa, ws2, out[layer])
+            else:
+                flux.attn_decode(q[layer], kc[layer], vc[layer], seqlens, route, layer, rp, ci, sa, ws,
+                                 out[layer])
+
+    for _ in range(2):
+        step_compact()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.decode_steps):
+        step_compact()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    compact_ms = e0.elapsed_time(e1) / args.decode_steps
+    full_cache_gib = nl * 2 * n_seq * hkv * ctx * d * 2 / 2**30
+    mixed_cache_gib = (len(sa_set) * 2 * n_seq * hkv * flux.kv_rows(ctx, sa, compact=True) * d * 2
+                       + (nl - len(sa_set)) * 2 * n_seq * hkv * ctx * d * 2) / 2**30
+    log(f"decode step with compact SA caches {compact_ms:.3f} ms; caches {full_cache_gib:.1f} GiB -> "
+        f"{mixed_cache_gib:.1f} GiB")
+    del cmp_caches
     fa_layers = [i for i in range(nl) if int(route_vec[i]) == 1]
     sa_layers = [i for i in range(nl) if int(route_vec[i]) == 0]
     sa_keys = (wl.sink_blocks + wl.local_blocks) * wl.block_size
@@ -558,6 +590,8 @@ def run_decode(args, flux, syn, dev, stream, log):
         "graph_ms_per_step": round(graph_ms, 4),
         "graph_tok_s": round(n_seq / (graph_ms * 1e-3), 1),
         "graph_gbs": round(step_bytes / (graph_ms * 1e-3) / 1e9, 1),
+        "compact_sa_ms_per_step": round(compact_ms, 4),
+        "cache_gib_full": round(full_cache_gib, 2), "cache_gib_compact_sa": round(mixed_cache_gib, 2),
         "fa_layer_ms": round(fa_ms, 4), "sa_layer_ms": round(sa_ms, 4),
         "bytes_per_step": step_bytes,
         "roofline": {"kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",

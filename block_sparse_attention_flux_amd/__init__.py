@@ -25,6 +25,7 @@ _LIB = _lib.load()
 __all__ = [
     "SAParams", "FluxError", "route", "route_workspace_size", "mask_blocks", "mask_nnz", "build_block_mask",
     "attn_prefill", "decode_workspace_size", "decode_workspace", "attn_decode", "status_str",
+    "kv_rows", "kv_cache", "kv_store_prefill", "kv_append", "attn_decode_sa_compact",
     "probe_mfma", "probe_read",
 ]
 
@@ -190,6 +191,81 @@ def attn_decode(q, k_cache, v_cache, seqlens, route, layer, row_ptr, col_idx, sa
         row_ptr.numel() - 1, sa.c(), _ptr(workspace, None, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(code, "flux_attn_decode")
+    return out
+
+
+# ---------------------------------------------------------------- K/V caches
+
+
+def kv_rows(max_len, sa, compact=False):
+    """Rows per (sequence, kv head) of a full or compact cache (flux_kv_rows)."""
+    n = _LIB.flux_kv_rows(int(max_len), sa.c(), int(bool(compact)))
+    if n < 0:
+        _check(int(n), "flux_kv_rows")
+    return int(n)
+
+
+def kv_cache(n_seq, hkv, head_dim, max_len, sa, compact=False, device="cuda"):
+    """A zero-filled (K, V) cache pair [n_seq][hkv][rows][head_dim] bf16."""
+    shape = (n_seq, hkv, kv_rows(max_len, sa, compact), head_dim)
+    return (torch.zeros(shape, dtype=torch.bfloat16, device=device),
+            torch.zeros(shape, dtype=torch.bfloat16, device=device))
+
+
+def _cache_args(k_cache, v_cache, max_len, sa, compact):
+    n_seq, hkv, rows, d = k_cache.shape
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    if rows != kv_rows(max_len, sa, compact):
+        raise ValueError(f"cache has {rows} rows per head, the layout needs {kv_rows(max_len, sa, compact)}")
+    return n_seq, hkv, d
+
+
+def kv_store_prefill(k, v, cu_seqlens, max_seqlen, k_cache, v_cache, max_len, sa, compact=False):
+    """Prompts' K/V rows into decode caches (flux_kv_store_prefill)."""
+    n_seq, hkv, d = _cache_args(k_cache, v_cache, max_len, sa, compact)
+    if k.shape[1:] != (hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [T][hkv][head_dim] like the caches")
+    code = _LIB.flux_kv_store_prefill(
+        _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"),
+        _ptr(cu_seqlens, torch.int32, "cu_seqlens"), cu_seqlens.numel() - 1, int(max_seqlen), hkv, d,
+        _ptr(k_cache, torch.bfloat16, "k_cache"), _ptr(v_cache, torch.bfloat16, "v_cache"),
+        int(max_len), int(bool(compact)), sa.c(), _stream(k.device))
+    _check(code, "flux_kv_store_prefill")
+
+
+def kv_append(k_new, v_new, seqlens, k_cache, v_cache, max_len, sa, compact=False):
+    """One new row per sequence at position seqlens[b] - 1 (flux_kv_append)."""
+    n_seq, hkv, d = _cache_args(k_cache, v_cache, max_len, sa, compact)
+    if k_new.shape != (n_seq, hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [n_seq][hkv][head_dim]")
+    code = _LIB.flux_kv_append(
+        _ptr(k_new, torch.bfloat16, "k_new"), _ptr(v_new, torch.bfloat16, "v_new"),
+        _ptr(seqlens, torch.int32, "seqlens"), n_seq, hkv, d,
+        _ptr(k_cache, torch.bfloat16, "k_cache"), _ptr(v_cache, torch.bfloat16, "v_cache"),
+        int(max_len), int(bool(compact)), sa.c(), _stream(k_new.device))
+    _check(code, "flux_kv_append")
+
+
+def attn_decode_sa_compact(q, k_cache, v_cache, seqlens, max_len, row_ptr, col_idx, sa,
+                           workspace=None, out=None, softmax_scale=None):
+    """One SA decode step of one layer over compact caches (flux_attn_decode_sa_compact)."""
+    n_seq, hq, d = q.shape
+    _, hkv, _ = _cache_args(k_cache, v_cache, max_len, sa, True)
+    if out is None:
+        out = torch.empty_like(q)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = decode_workspace(n_seq, hq, hkv, d, max_len, q.device)
+    code = _LIB.flux_attn_decode_sa_compact(
+        _ptr(q, torch.bfloat16, "q"), _ptr(k_cache, torch.bfloat16, "k_cache"),
+        _ptr(v_cache, torch.bfloat16, "v_cache"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(seqlens, torch.int32, "seqlens"), n_seq, int(max_len), hq, hkv, d, float(softmax_scale),
+        _ptr(row_ptr, torch.int32, "row_ptr"), _ptr(col_idx, torch.int32, "col_idx"),
+        row_ptr.numel() - 1, sa.c(), _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(code, "flux_attn_decode_sa_compact")
     return out
 
 

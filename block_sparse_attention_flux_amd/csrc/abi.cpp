@@ -172,6 +172,109 @@ flux_status flux_attn_decode(const uint16_t* q, const uint16_t* k_cache, const u
   dp.n_seq = n_seq; dp.max_len = max_len; dp.hq = hq; dp.hkv = hkv; dp.head_dim = head_dim;
   dp.n_layers = n_layers; dp.layer = layer; dp.mask_blocks = mask_blocks;
   dp.block_size = p.block_size; dp.nsplit = ns; dp.scale = softmax_scale;
+  dp.cache_rows = max_len; dp.compact = 0;
+  dp.sink_blocks = p.sink_blocks; dp.local_blocks = p.local_blocks;
+  return from_hip(flux::launch_decode(dp, static_cast<hipStream_t>(stream)));
+}
+
+int64_t flux_kv_rows(int32_t max_len, flux_sa_params p, int32_t compact) {
+  if (max_len < 1 || (compact != 0 && compact != 1)) return FLUX_ERR_INVALID_ARG;
+  if (!compact) return max_len;
+  if (!sa_params_ok(p) || p.block_size < 1) return FLUX_ERR_INVALID_ARG;
+  return flux::compact_rows(p.block_size, p.sink_blocks, p.local_blocks);
+}
+
+namespace {
+// Checks shared by the two cache writers; on success *rows is the cache's
+// rows per (sequence, kv head).
+flux_status check_cache(int32_t hkv, int32_t head_dim, int32_t max_len, int32_t compact,
+                        flux_sa_params p, int32_t* rows) {
+  if (hkv < 1 || max_len < 1 || (compact != 0 && compact != 1)) return FLUX_ERR_INVALID_ARG;
+  if (!head_dim_supported(head_dim)) return FLUX_ERR_UNSUPPORTED;
+  if (compact) {
+    if (!sa_params_ok(p)) return FLUX_ERR_INVALID_ARG;
+    if (!block_supported(p.block_size)) return FLUX_ERR_UNSUPPORTED;
+    const int64_t r = flux::compact_rows(p.block_size, p.sink_blocks, p.local_blocks);
+    if (r > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
+    *rows = static_cast<int32_t>(r);
+  } else {
+    *rows = max_len;
+  }
+  return FLUX_OK;
+}
+}  // namespace
+
+flux_status flux_kv_store_prefill(const uint16_t* k, const uint16_t* v, const int32_t* cu_seqlens,
+                                  int32_t n_req, int32_t max_seqlen, int32_t hkv, int32_t head_dim,
+                                  uint16_t* k_cache, uint16_t* v_cache, int32_t max_len,
+                                  int32_t compact, flux_sa_params p, void* stream) {
+  if (k == nullptr || v == nullptr || cu_seqlens == nullptr || k_cache == nullptr ||
+      v_cache == nullptr)
+    return FLUX_ERR_INVALID_ARG;
+  if (n_req < 1 || max_seqlen < 1 || max_seqlen > max_len) return FLUX_ERR_INVALID_ARG;
+  int32_t rows = 0;
+  const flux_status st = check_cache(hkv, head_dim, max_len, compact, p, &rows);
+  if (st != FLUX_OK) return st;
+  if (n_req > 65535) return FLUX_ERR_UNSUPPORTED;  // grid y dimension
+  return from_hip(flux::launch_kv_store_prefill(k, v, cu_seqlens, n_req, max_seqlen, hkv, head_dim,
+                                                k_cache, v_cache, rows, max_len, compact,
+                                                p.block_size, p.sink_blocks, p.local_blocks,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+flux_status flux_kv_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* seqlens,
+                           int32_t n_seq, int32_t hkv, int32_t head_dim, uint16_t* k_cache,
+                           uint16_t* v_cache, int32_t max_len, int32_t compact, flux_sa_params p,
+                           void* stream) {
+  if (k_new == nullptr || v_new == nullptr || seqlens == nullptr || k_cache == nullptr ||
+      v_cache == nullptr)
+    return FLUX_ERR_INVALID_ARG;
+  if (n_seq < 1) return FLUX_ERR_INVALID_ARG;
+  int32_t rows = 0;
+  const flux_status st = check_cache(hkv, head_dim, max_len, compact, p, &rows);
+  if (st != FLUX_OK) return st;
+  if (static_cast<int64_t>(n_seq) * hkv > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
+  return from_hip(flux::launch_kv_append(k_new, v_new, seqlens, n_seq, hkv, head_dim, k_cache,
+                                         v_cache, rows, max_len, compact, p.block_size,
+                                         p.sink_blocks, p.local_blocks,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+flux_status flux_attn_decode_sa_compact(const uint16_t* q, const uint16_t* k_cache,
+                                        const uint16_t* v_cache, uint16_t* out,
+                                        const int32_t* seqlens, int32_t n_seq, int32_t max_len,
+                                        int32_t hq, int32_t hkv, int32_t head_dim,
+                                        float softmax_scale, const int32_t* mask_row_ptr,
+                                        const int32_t* mask_col_idx, int32_t mask_blocks,
+                                        flux_sa_params p, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr ||
+      seqlens == nullptr)
+    return FLUX_ERR_INVALID_ARG;
+  if (out == q) return FLUX_ERR_INVALID_ARG;
+  if (n_seq < 1 || max_len < 1) return FLUX_ERR_INVALID_ARG;
+  static const uint8_t kSa = 0;  // route placeholder for the shared checks (never read)
+  const flux_status st = check_attn_common(hq, hkv, head_dim, softmax_scale, &kSa, 1, 0,
+                                           mask_row_ptr, mask_col_idx, mask_blocks, max_len, p);
+  if (st != FLUX_OK) return st;
+  int32_t rows = 0;
+  const flux_status sc = check_cache(hkv, head_dim, max_len, 1, p, &rows);
+  if (sc != FLUX_OK) return sc;
+  const int32_t ns = flux::decode_splits(n_seq, hkv, max_len);
+  if (static_cast<int64_t>(n_seq) * hkv * ns > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
+  const size_t need = flux_attn_decode_workspace_size(n_seq, hq, hkv, head_dim, max_len);
+  if (ns > 1 && (workspace == nullptr || workspace_bytes < need)) return FLUX_ERR_WORKSPACE;
+  flux::DecodeParams dp{};
+  dp.q = q; dp.k_cache = k_cache; dp.v_cache = v_cache; dp.out = out;
+  dp.seqlens = seqlens; dp.route = nullptr; dp.row_ptr = mask_row_ptr; dp.col_idx = mask_col_idx;
+  const size_t slots = static_cast<size_t>(n_seq) * hq * ns;
+  dp.part_o = static_cast<float*>(workspace);
+  dp.part_ml = workspace != nullptr ? static_cast<float*>(workspace) + slots * head_dim : nullptr;
+  dp.n_seq = n_seq; dp.max_len = max_len; dp.hq = hq; dp.hkv = hkv; dp.head_dim = head_dim;
+  dp.n_layers = 1; dp.layer = 0; dp.mask_blocks = mask_blocks;
+  dp.block_size = p.block_size; dp.nsplit = ns; dp.scale = softmax_scale;
+  dp.cache_rows = rows; dp.compact = 1;
+  dp.sink_blocks = p.sink_blocks; dp.local_blocks = p.local_blocks;
   return from_hip(flux::launch_decode(dp, static_cast<hipStream_t>(stream)));
 }
 

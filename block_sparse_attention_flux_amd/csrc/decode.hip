@@ -66,7 +66,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   const int group = p.hq / p.hkv;
 
   const int N = min(max(p.seqlens[b], 1), p.max_len);
-  const bool fa = p.route[static_cast<int64_t>(b) * p.n_layers + p.layer] != 0;
+  // a compact cache only holds an SA layer's rows (and comes without a route)
+  bool fa = false;
+  if (!p.compact) fa = p.route[static_cast<int64_t>(b) * p.n_layers + p.layer] != 0;
   const int B = p.block_size;
   const int mrow = min((N - 1) / B, p.mask_blocks - 1);
   int rp0 = 0, U;
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   const int u0 = split * per;
   const int u1 = min(U, u0 + per);
 
-  const size_t cache_head = static_cast<size_t>(p.max_len) * D;
+  const size_t cache_head = static_cast<size_t>(p.cache_rows) * D;
   const uint16_t* kc = p.k_cache + (static_cast<size_t>(b) * p.hkv + g) * cache_head;
   const uint16_t* vc = p.v_cache + (static_cast<size_t>(b) * p.hkv + g) * cache_head;
 
@@ -90,6 +92,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
     if (fa) return u;
     const int blk = min(max(p.col_idx[rp0 + u / B], 0), mrow);
     return blk * B + u % B;
+  };
+  // cache row of key position k: the position itself in a full cache; in a
+  // compact cache the sink rows come first and every later block has its
+  // ring slot (block j at rows sink*B + (j % local)*B).  A 32-key chunk never
+  // crosses a block, so its rows are consecutive either way.
+  auto cache_row = [&](int k) -> int {
+    if (!p.compact) return k;
+    const int blk = k / B;
+    return blk < p.sink_blocks ? k : (p.sink_blocks + blk % p.local_blocks) * B + k % B;
   };
 
   // ---- Q^T operand: column n = l16 is query head g*group + l16 (zero beyond the group)
@@ -121,12 +132,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   auto load_chunk = [&](int u, KRegs& kr, VRegs& vr, int& k0, int& limit) {
     k0 = chunk_key(u);
     limit = min(k0 + min(u1 - u, kChunk), N);
+    const int row0 = cache_row(k0) - k0;  // row of key k is row0 + k within this chunk
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int key = k0 + mt * 16 + l16;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
-        kr[mt][ks] = key < limit ? ld16(kc + static_cast<size_t>(key) * D + ks * 32 + quarter * 8)
+        kr[mt][ks] = key < limit ? ld16(kc + static_cast<size_t>(row0 + key) * D + ks * 32 + quarter * 8)
                                  : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
@@ -136,7 +148,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int key = k0 + qd * 4 + kk;
-        vr[j][kk] = key < limit ? ld16(vc + static_cast<size_t>(key) * D + c * 8)
+        vr[j][kk] = key < limit ? ld16(vc + static_cast<size_t>(row0 + key) * D + c * 8)
                                 : u32x4{0, 0, 0, 0};
       }
     }

@@ -34,8 +34,32 @@ struct DecodeParams {
   float* part_ml;  // [n_seq][hq][nsplit][2]
   int32_t n_seq, max_len, hq, hkv, head_dim, n_layers, layer, mask_blocks;
   int32_t block_size, nsplit;
+  int32_t cache_rows;                 // rows per (sequence, kv head) in the caches
+  int32_t compact;                    // 1: SA cache of sink rows + a ring of window rows
+  int32_t sink_blocks, local_blocks;  // the SA pattern (compact row mapping)
   float scale;
 };
+
+// Rows per (sequence, kv head) of a compact SA cache: sink + window blocks.
+inline int64_t compact_rows(int32_t block_size, int32_t sink_blocks, int32_t local_blocks) {
+  return static_cast<int64_t>(sink_blocks + local_blocks) * block_size;
+}
+
+// K/V cache writes (kvcache.hip).  Caches are [n_seq][hkv][cache_rows][d].
+// store_prefill: rows of packed prompts k/v [T][hkv][d] (by cu_seqlens) at
+// their positions; with compact set, only positions below sink*B and the
+// last local*B positions of each prompt, at their compact rows.
+hipError_t launch_kv_store_prefill(const uint16_t* k, const uint16_t* v, const int32_t* cu_seqlens,
+                                   int32_t n_req, int32_t max_seqlen, int32_t hkv, int32_t head_dim,
+                                   uint16_t* k_cache, uint16_t* v_cache, int32_t cache_rows,
+                                   int32_t max_len, int32_t compact, int32_t block_size,
+                                   int32_t sink_blocks, int32_t local_blocks, hipStream_t s);
+// append: row of k_new/v_new [n_seq][hkv][d] at position seqlens[b] - 1.
+hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* seqlens,
+                            int32_t n_seq, int32_t hkv, int32_t head_dim, uint16_t* k_cache,
+                            uint16_t* v_cache, int32_t cache_rows, int32_t max_len, int32_t compact,
+                            int32_t block_size, int32_t sink_blocks, int32_t local_blocks,
+                            hipStream_t s);
 
 hipError_t launch_build_mask(int32_t nb, int32_t sink, int32_t local, uint8_t* mask,
                              int32_t* row_ptr, int32_t* col_idx, hipStream_t s);

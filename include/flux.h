@@ -178,6 +178,77 @@ flux_status flux_attn_decode(const uint16_t* q, const uint16_t* k_cache,
                              flux_sa_params p, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * K/V caches for decode, and the compact SA-layer cache.
+ * The route is decided once at prefill and reused by every decode step, and
+ * SA layers read only their sink and window keys, never the rest of the
+ * history (technical summary, section 2, deployment paragraph).  A cache is
+ * [n_seq][hkv][rows][head_dim] bf16 with rows = flux_kv_rows(max_len, p,
+ * compact):
+ *   full    (compact = 0): rows = max_len, position t at row t;
+ *   compact (compact = 1): rows = (sink_blocks + local_blocks) * block_size;
+ *           positions t < sink_blocks*B at row t, every later position t at
+ *           row sink_blocks*B + t mod (local_blocks*B) (a ring of the last
+ *           local_blocks blocks).  This holds every key an SA decode step
+ *           reads with the mask of flux_build_block_mask for the same p, and
+ *           nothing else: at 32K context with 1 sink and 16 local blocks of
+ *           128, 2176 rows instead of 32768.
+ * Positions at or beyond max_len are never written (the writers skip them).
+ */
+
+/* Rows per (sequence, kv head) of a cache [host]; negative flux_status on
+ * invalid input (compact must be 0 or 1; p is only used when compact). */
+int64_t flux_kv_rows(int32_t max_len, flux_sa_params p, int32_t compact);
+
+/*
+ * flux_kv_store_prefill -- the prompts' K/V rows into decode caches.
+ * k, v       [device] bf16 [T][hkv][head_dim], packed by cu_seqlens (the same
+ *            tensors flux_attn_prefill reads); cu_seqlens [device] int32
+ *            [n_req+1]; request r becomes sequence r of the caches.
+ * k_cache, v_cache [device] bf16 [n_req][hkv][rows][head_dim]; full caches get
+ *            every prompt position, compact caches the sink positions and the
+ *            last local_blocks*B positions of each prompt.
+ * Requires max_seqlen <= max_len; head_dim in {64, 128}; compact caches need
+ * block_size in {64, 128}.  Rows not written keep their contents.
+ */
+flux_status flux_kv_store_prefill(const uint16_t* k, const uint16_t* v,
+                                  const int32_t* cu_seqlens, int32_t n_req,
+                                  int32_t max_seqlen, int32_t hkv, int32_t head_dim,
+                                  uint16_t* k_cache, uint16_t* v_cache, int32_t max_len,
+                                  int32_t compact, flux_sa_params p, void* stream);
+
+/*
+ * flux_kv_append -- one new K/V row per sequence (a decode step's token).
+ * k_new, v_new [device] bf16 [n_seq][hkv][head_dim]; the row is written at
+ * position seqlens[b] - 1, i.e. seqlens already counts the new token (the
+ * convention of flux_attn_decode).  Sequences with seqlens[b] < 1 or
+ * seqlens[b] > max_len are left alone.
+ */
+flux_status flux_kv_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* seqlens,
+                           int32_t n_seq, int32_t hkv, int32_t head_dim, uint16_t* k_cache,
+                           uint16_t* v_cache, int32_t max_len, int32_t compact,
+                           flux_sa_params p, void* stream);
+
+/*
+ * flux_attn_decode_sa_compact -- flux_attn_decode for an SA layer whose caches
+ * are compact.  Every sequence is treated as SA (a compact cache cannot serve
+ * FA, so there is no route argument); keys are those of mask row
+ * (seqlens[b] - 1) / block_size, read from their compact rows.  max_len is the
+ * logical capacity (seqlens are clamped to it, the mask needs ceil(max_len /
+ * block_size) rows and the workspace is flux_attn_decode_workspace_size(...,
+ * max_len), as for flux_attn_decode); the result is bit-identical to
+ * flux_attn_decode on full caches with the same keys.  The CSR must be the
+ * flux_build_block_mask pattern of the same p.
+ */
+flux_status flux_attn_decode_sa_compact(const uint16_t* q, const uint16_t* k_cache,
+                                        const uint16_t* v_cache, uint16_t* out,
+                                        const int32_t* seqlens, int32_t n_seq, int32_t max_len,
+                                        int32_t hq, int32_t hkv, int32_t head_dim,
+                                        float softmax_scale, const int32_t* mask_row_ptr,
+                                        const int32_t* mask_col_idx, int32_t mask_blocks,
+                                        flux_sa_params p, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

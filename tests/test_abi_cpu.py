@@ -31,7 +31,7 @@ def declared_symbols(header=HEADER):
 
 def test_exports_every_declared_symbol():
     syms = declared_symbols()
-    assert len(syms) == 9, syms
+    assert len(syms) == 13, syms
     raw = ctypes.CDLL(LIB)
     for s in syms:
         assert hasattr(raw, s), s
@@ -158,3 +158,53 @@ def test_binding_rejects_host_tensors():
     assert flux.mask_nnz(32768, flux.SAParams(128, 1, 16)) == 4216
     with pytest.raises(ValueError):
         flux.mask_nnz(0, flux.SAParams(128, 1, 16))
+
+
+def test_kv_rows_and_cache_validation():
+    sa = SA(128, 1, 16)
+    assert lib.flux_kv_rows(32768, sa, 0) == 32768
+    assert lib.flux_kv_rows(32768, sa, 1) == 17 * 128
+    assert lib.flux_kv_rows(5000, SA(64, 0, 3), 1) == 3 * 64
+    assert lib.flux_kv_rows(0, sa, 0) == _lib.FLUX_ERR_INVALID_ARG
+    assert lib.flux_kv_rows(100, sa, 2) == _lib.FLUX_ERR_INVALID_ARG
+    assert lib.flux_kv_rows(100, SA(128, 1, 0), 1) == _lib.FLUX_ERR_INVALID_ARG
+
+    def store(k=FAKE, cu=FAKE, n_req=2, max_s=100, hkv=8, d=128, max_len=200, compact=0, p=sa):
+        return lib.flux_kv_store_prefill(k, FAKE, cu, n_req, max_s, hkv, d, FAKE, FAKE, max_len,
+                                         compact, p, NULL)
+    assert store(k=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert store(cu=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert store(max_s=300) == _lib.FLUX_ERR_INVALID_ARG          # prompt longer than the cache
+    assert store(d=96) == _lib.FLUX_ERR_UNSUPPORTED
+    assert store(compact=3) == _lib.FLUX_ERR_INVALID_ARG
+    assert store(compact=1, p=SA(96, 1, 2)) == _lib.FLUX_ERR_UNSUPPORTED
+    assert store(compact=1, p=SA(128, -1, 2)) == _lib.FLUX_ERR_INVALID_ARG
+    assert store(n_req=70000, max_len=200) == _lib.FLUX_ERR_UNSUPPORTED
+
+    def append(kn=FAKE, sl=FAKE, n=4, hkv=8, d=128, max_len=100, compact=0, p=sa):
+        return lib.flux_kv_append(kn, FAKE, sl, n, hkv, d, FAKE, FAKE, max_len, compact, p, NULL)
+    assert append(kn=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert append(sl=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert append(n=0) == _lib.FLUX_ERR_INVALID_ARG
+    assert append(hkv=0) == _lib.FLUX_ERR_INVALID_ARG
+    assert append(d=80) == _lib.FLUX_ERR_UNSUPPORTED
+    assert append(compact=1, p=SA(128, 1, 0)) == _lib.FLUX_ERR_INVALID_ARG
+
+
+def test_compact_decode_validation():
+    sa = SA(128, 1, 16)
+    ws = lib.flux_attn_decode_workspace_size(16, 32, 8, 128, 32768)
+
+    def dec(q=FAKE, out=FAKE, n=16, max_len=32768, hq=32, hkv=8, d=128, scale=0.088, rp=FAKE,
+            mb=256, p=sa, w=FAKE, wsb=ws):
+        return lib.flux_attn_decode_sa_compact(q, FAKE, FAKE, out, FAKE, n, max_len, hq, hkv, d,
+                                               scale, rp, FAKE, mb, p, w, wsb, NULL)
+    assert dec(q=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(out=FAKE, q=FAKE) == _lib.FLUX_ERR_INVALID_ARG    # out aliases q
+    assert dec(rp=NULL, out=ctypes.c_void_p(0x2000)) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(hq=30, out=ctypes.c_void_p(0x2000)) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(d=96, out=ctypes.c_void_p(0x2000)) == _lib.FLUX_ERR_UNSUPPORTED
+    assert dec(mb=255, out=ctypes.c_void_p(0x2000)) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(p=SA(128, 1, 0), out=ctypes.c_void_p(0x2000)) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(w=NULL, out=ctypes.c_void_p(0x2000)) == _lib.FLUX_ERR_WORKSPACE
+    assert dec(wsb=ws - 4, out=ctypes.c_void_p(0x2000)) == _lib.FLUX_ERR_WORKSPACE

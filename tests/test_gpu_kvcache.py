@@ -1,0 +1,97 @@
+"""GPU tests of the decode caches through the C ABI binding: the prompt store
+and the per-step append are exact byte moves, and SA decode over a compact
+cache (sink rows + a ring of the window) is bit-identical to SA decode over
+the full cache, step after step, across block boundaries and ring wrap-round;
+sampled steps are also checked against the float64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import inputs as syn
+from tests.flux_testlib import assert_attn_close, ensure_built
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    ensure_built()
+    import block_sparse_attention_flux_amd as flux
+    from tests.test_gpu_parity import f32, say
+else:  # collected on CPU only to be deselected
+    flux = None
+
+DEV = "cuda"
+
+
+def packed(lens, hkv, d, g):
+    T = sum(lens)
+    return syn.normal((T, hkv, d), g, DEV), syn.normal((T, hkv, d), g, DEV)
+
+
+def test_store_and_append_full_cache_exact():
+    say("kv store/append full")
+    lens, hkv, d, max_len = [5, 130, 1000], 2, 128, 1100
+    sa = flux.SAParams(128, 1, 2)
+    g = syn.generator(501, DEV)
+    k, v = packed(lens, hkv, d, g)
+    cu = syn.cu_seqlens(lens, DEV)
+    kc, vc = flux.kv_cache(len(lens), hkv, d, max_len, sa)
+    flux.kv_store_prefill(k, v, cu, max(lens), kc, vc, max_len, sa)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    new = []
+    for t in range(5):
+        sl = sl + 1
+        kn, vn = syn.normal((len(lens), hkv, d), g, DEV), syn.normal((len(lens), hkv, d), g, DEV)
+        flux.kv_append(kn, vn, sl, kc, vc, max_len, sa)
+        new.append((kn, vn))
+    torch.cuda.synchronize()
+    c = [0] + list(np.cumsum(lens))
+    for b, S in enumerate(lens):
+        assert torch.equal(kc[b, :, :S], k[c[b]:c[b + 1]].transpose(0, 1))
+        assert torch.equal(vc[b, :, :S], v[c[b]:c[b + 1]].transpose(0, 1))
+        for t, (kn, vn) in enumerate(new):
+            assert torch.equal(kc[b, :, S + t], kn[b]) and torch.equal(vc[b, :, S + t], vn[b])
+        assert not kc[b, :, S + 5:].any() and not vc[b, :, S + 5:].any()  # untouched rows
+
+
+@pytest.mark.parametrize("case", [
+    # lens, hq, hkv, d, B, s, w, steps
+    ([70, 1000, 4100], 8, 2, 128, 64, 1, 3, 300),
+    ([129, 2500], 4, 4, 64, 128, 2, 4, 300),
+    ([1, 640, 3000], 16, 1, 128, 64, 0, 2, 200),
+])
+def test_compact_sa_decode_matches_full(case):
+    lens, hq, hkv, d, B, s, w, steps = case
+    say(f"compact decode {case}")
+    n = len(lens)
+    max_len = max(lens) + steps
+    sa = flux.SAParams(B, s, w)
+    g = syn.generator(700 + d + B, DEV)
+    k, v = packed(lens, hkv, d, g)
+    cu = syn.cu_seqlens(lens, DEV)
+    kf, vf = flux.kv_cache(n, hkv, d, max_len, sa)
+    kcp, vcp = flux.kv_cache(n, hkv, d, max_len, sa, compact=True)
+    assert kcp.shape[2] == (s + w) * B
+    flux.kv_store_prefill(k, v, cu, max(lens), kf, vf, max_len, sa)
+    flux.kv_store_prefill(k, v, cu, max(lens), kcp, vcp, max_len, sa, compact=True)
+    _, rp, ci = flux.build_block_mask(max_len, sa, dense=False)
+    route = torch.zeros((n, 1), dtype=torch.uint8, device=DEV)  # every sequence SA
+    ws_full = flux.decode_workspace(n, hq, hkv, d, max_len, DEV)
+    ws_cmp = flux.decode_workspace(n, hq, hkv, d, max_len, DEV)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    m = oracle.block_mask(oracle.num_blocks(max_len, B), s, w)
+    check_at = {0, steps // 2, steps - 1}
+    for t in range(steps):
+        sl = sl + 1
+        kn, vn = syn.normal((n, hkv, d), g, DEV), syn.normal((n, hkv, d), g, DEV)
+        flux.kv_append(kn, vn, sl, kf, vf, max_len, sa)
+        flux.kv_append(kn, vn, sl, kcp, vcp, max_len, sa, compact=True)
+        q = syn.normal((n, hq, d), g, DEV)
+        full = flux.attn_decode(q, kf, vf, sl, route, 0, rp, ci, sa, ws_full)
+        cmp_ = flux.attn_decode_sa_compact(q, kcp, vcp, sl, max_len, rp, ci, sa, ws_cmp)
+        torch.cuda.synchronize()
+        assert torch.equal(full, cmp_), f"step {t}: compact and full caches differ"
+        if t in check_at:
+            ref = oracle.attention_decode(f32(q), f32(kf), f32(vf), sl.cpu().numpy(), False, m, B)
+            assert_attn_close(f32(cmp_), ref, f"compact decode step {t}")
