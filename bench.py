@@ -210,6 +210,8 @@ def main():
             "traffic": None,
         },
     }
+    result["head_routing"] = head_routing(flux, q, k, v, cu, S, row_ptr, col_idx, sa, fa_ms, sa_ms,
+                                          fa_flops + sa_flops, stream, log)
     att = attainable(flux, dev, stream, log)
     result["attainable"] = att
     result["roofline"]["frac_attainable"] = round(pre_tflops / att["mfma_tflops"], 4)
@@ -240,6 +242,46 @@ def main():
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def head_routing(flux, q, k, v, cu, S, row_ptr, col_idx, sa, fa_ms, sa_ms, pair_flops, stream, log):
+    """Layer-level against head-level routing on the same 32K inputs and the
+    same total work: the layer-routed pair is one FA layer + one SA layer; the
+    head-routed pair is two layers that each send half of the kv heads to FA
+    and the other half to SA (complementary halves).  The pages' case for
+    layer-level routing is that head-level decisions leave the GPU waiting on
+    the heaviest heads (load imbalance, long tails)."""
+    import torch
+
+    hkv = k.shape[1]
+    out = torch.empty_like(q)
+
+    def timed(route, layer, reps=5):
+        flux.attn_prefill(q, k, v, cu, S, route, layer, row_ptr, col_idx, sa, out=out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            flux.attn_prefill(q, k, v, cu, S, route, layer, row_ptr, col_idx, sa, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {"layer_level_pair_ms": round(fa_ms + sa_ms, 4)}
+    patterns = {"halves": [1 if g < hkv // 2 else 0 for g in range(hkv)],
+                "alternate": [1 - g % 2 for g in range(hkv)]}
+    for name, pat in patterns.items():
+        r = torch.tensor([[pat, [1 - x for x in pat]]], dtype=torch.uint8, device=q.device)
+        ms = timed(r, 0) + timed(r, 1)
+        res[f"head_level_pair_ms_{name}"] = round(ms, 4)
+        res[f"slowdown_{name}"] = round(ms / (fa_ms + sa_ms), 3)
+    log(f"head routing: layer-level pair {fa_ms + sa_ms:.3f} ms, head-level pair "
+        f"{res['head_level_pair_ms_halves']:.3f} ms (halves) / {res['head_level_pair_ms_alternate']:.3f} ms "
+        f"(alternate) for the same {pair_flops / 1e12:.2f} TFLOP")
+    res["note"] = ("head-routed launches deal every kv-head group to every XCD (a layer-routed launch "
+                   "keeps whole groups on one XCD for L2 locality; the same interleaving costs a "
+                   "layer-routed FA layer ~4 % and an SA layer ~15 %)")
+    return res
 
 
 def attainable(flux, dev, stream, log):

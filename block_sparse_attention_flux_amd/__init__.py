@@ -137,22 +137,33 @@ def build_block_mask(seqlen, sa, device="cuda", dense=True):
     return mask, row_ptr, col_idx[:nnz]
 
 
+def _route_fn(route, hkv, layer_fn, head_fn, what):
+    """route [n][L] -> one decision per layer; [n][L][hkv] -> one per kv head."""
+    if route.dim() == 2:
+        return layer_fn
+    if route.dim() == 3 and route.shape[2] == hkv:
+        return head_fn
+    raise ValueError(f"{what}: route must be [n][n_layers] or [n][n_layers][hkv]")
+
+
 def attn_prefill(q, k, v, cu_seqlens, max_seqlen, route, layer, row_ptr, col_idx, sa,
                  out=None, softmax_scale=None):
-    """One routed attention layer over packed prompts (flux_attn_prefill)."""
+    """One routed attention layer over packed prompts (flux_attn_prefill, or
+    flux_attn_prefill_heads for a per-kv-head route [n_req][n_layers][hkv])."""
     T, hq, d = q.shape
     hkv = k.shape[1]
     if k.shape != (T, hkv, d) or v.shape != (T, hkv, d):
         raise ValueError("k and v must be [T][hkv][head_dim] like q")
+    fn = _route_fn(route, hkv, _LIB.flux_attn_prefill, _LIB.flux_attn_prefill_heads, "attn_prefill")
     if out is None:
         out = torch.empty_like(q)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
-    code = _LIB.flux_attn_prefill(
+    code = fn(
         _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"),
         _ptr(out, torch.bfloat16, "out"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
         cu_seqlens.numel() - 1, int(max_seqlen), hq, hkv, d, float(softmax_scale),
-        _ptr(route, torch.uint8, "route"), route.shape[-1], int(layer),
+        _ptr(route, torch.uint8, "route"), route.shape[1], int(layer),
         _ptr(row_ptr, torch.int32, "row_ptr"), _ptr(col_idx, torch.int32, "col_idx"),
         row_ptr.numel() - 1, sa.c(), _stream(q.device))
     _check(code, "flux_attn_prefill")
@@ -171,22 +182,24 @@ def decode_workspace(n_seq, hq, hkv, head_dim, max_len, device="cuda"):
 
 def attn_decode(q, k_cache, v_cache, seqlens, route, layer, row_ptr, col_idx, sa,
                 workspace=None, out=None, softmax_scale=None):
-    """One split-KV decode step of one layer (flux_attn_decode)."""
+    """One split-KV decode step of one layer (flux_attn_decode, or
+    flux_attn_decode_heads for a per-kv-head route [n_seq][n_layers][hkv])."""
     n_seq, hq, d = q.shape
     _, hkv, max_len, _ = k_cache.shape
     if k_cache.shape != (n_seq, hkv, max_len, d) or v_cache.shape != k_cache.shape:
         raise ValueError("caches must be [n_seq][hkv][max_len][head_dim]")
+    fn = _route_fn(route, hkv, _LIB.flux_attn_decode, _LIB.flux_attn_decode_heads, "attn_decode")
     if out is None:
         out = torch.empty_like(q)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
     if workspace is None:
         workspace = decode_workspace(n_seq, hq, hkv, d, max_len, q.device)
-    code = _LIB.flux_attn_decode(
+    code = fn(
         _ptr(q, torch.bfloat16, "q"), _ptr(k_cache, torch.bfloat16, "k_cache"),
         _ptr(v_cache, torch.bfloat16, "v_cache"), _ptr(out, torch.bfloat16, "out"),
         _ptr(seqlens, torch.int32, "seqlens"), n_seq, max_len, hq, hkv, d, float(softmax_scale),
-        _ptr(route, torch.uint8, "route"), route.shape[-1], int(layer),
+        _ptr(route, torch.uint8, "route"), route.shape[1], int(layer),
         _ptr(row_ptr, torch.int32, "row_ptr"), _ptr(col_idx, torch.int32, "col_idx"),
         row_ptr.numel() - 1, sa.c(), _ptr(workspace, None, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(q.device))

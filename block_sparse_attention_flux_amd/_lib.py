@@ -41,6 +41,10 @@ SIGNATURES = [
     ("flux_attn_decode_workspace_size", _S, [_I, _I, _I, _I, _I]),
     ("flux_attn_decode", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P, _P, _I,
                               SAParamsC, _P, _S, _P]),
+    ("flux_attn_prefill_heads", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P,
+                                     _P, _I, SAParamsC, _P]),
+    ("flux_attn_decode_heads", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P, _P,
+                                    _I, SAParamsC, _P, _S, _P]),
     ("flux_kv_rows", ctypes.c_int64, [_I, SAParamsC, _I]),
     ("flux_kv_store_prefill", _I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, SAParamsC, _P]),
     ("flux_kv_append", _I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, SAParamsC, _P]),

@@ -44,6 +44,87 @@ flux_status check_attn_common(int32_t hq, int32_t hkv, int32_t head_dim, float s
   return FLUX_OK;
 }
 
+flux_status attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                         const int32_t* cu_seqlens, int32_t n_req, int32_t max_seqlen, int32_t hq,
+                         int32_t hkv, int32_t head_dim, float softmax_scale, const uint8_t* route,
+                         int32_t n_layers, int32_t layer, const int32_t* mask_row_ptr,
+                         const int32_t* mask_col_idx, int32_t mask_blocks, flux_sa_params p,
+                         int32_t route_heads, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || cu_seqlens == nullptr)
+    return FLUX_ERR_INVALID_ARG;
+  if (out == q || out == k || out == v) return FLUX_ERR_INVALID_ARG;
+  if (n_req < 1 || max_seqlen < 1) return FLUX_ERR_INVALID_ARG;
+  const flux_status st = check_attn_common(hq, hkv, head_dim, softmax_scale, route, n_layers, layer,
+                                           mask_row_ptr, mask_col_idx, mask_blocks, max_seqlen, p);
+  if (st != FLUX_OK) return st;
+  const int64_t n_qt = (static_cast<int64_t>(max_seqlen) + p.block_size - 1) / p.block_size;
+  if (n_qt * hq * n_req > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
+  // K/V rows of one request are addressed with 32-bit byte offsets
+  if (static_cast<int64_t>(max_seqlen) * hkv * head_dim * 2 > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
+  flux::PrefillParams pp{};
+  pp.q = q; pp.k = k; pp.v = v; pp.out = out;
+  pp.cu_seqlens = cu_seqlens; pp.route = route;
+  pp.row_ptr = mask_row_ptr; pp.col_idx = mask_col_idx;
+  pp.n_req = n_req; pp.max_seqlen = max_seqlen; pp.hq = hq; pp.hkv = hkv;
+  pp.head_dim = head_dim; pp.n_layers = n_layers; pp.layer = layer;
+  pp.mask_blocks = mask_blocks; pp.block_size = p.block_size;
+  pp.sink_blocks = p.sink_blocks; pp.local_blocks = p.local_blocks;
+  pp.scale = softmax_scale;
+  pp.route_heads = route_heads;
+  return from_hip(flux::launch_prefill(pp, static_cast<hipStream_t>(stream)));
+}
+
+flux_status attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                        uint16_t* out, const int32_t* seqlens, int32_t n_seq, int32_t max_len,
+                        int32_t hq, int32_t hkv, int32_t head_dim, float softmax_scale,
+                        const uint8_t* route, int32_t n_layers, int32_t layer,
+                        const int32_t* mask_row_ptr, const int32_t* mask_col_idx,
+                        int32_t mask_blocks, flux_sa_params p, int32_t route_heads,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr ||
+      seqlens == nullptr)
+    return FLUX_ERR_INVALID_ARG;
+  if (out == q) return FLUX_ERR_INVALID_ARG;
+  if (n_seq < 1 || max_len < 1) return FLUX_ERR_INVALID_ARG;
+  const flux_status st = check_attn_common(hq, hkv, head_dim, softmax_scale, route, n_layers, layer,
+                                           mask_row_ptr, mask_col_idx, mask_blocks, max_len, p);
+  if (st != FLUX_OK) return st;
+  const int32_t ns = flux::decode_splits(n_seq, hkv, max_len);
+  if (static_cast<int64_t>(n_seq) * hkv * ns > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
+  const size_t need = flux_attn_decode_workspace_size(n_seq, hq, hkv, head_dim, max_len);
+  if (ns > 1 && (workspace == nullptr || workspace_bytes < need)) return FLUX_ERR_WORKSPACE;
+  flux::DecodeParams dp{};
+  dp.q = q; dp.k_cache = k_cache; dp.v_cache = v_cache; dp.out = out;
+  dp.seqlens = seqlens; dp.route = route; dp.row_ptr = mask_row_ptr; dp.col_idx = mask_col_idx;
+  const size_t slots = static_cast<size_t>(n_seq) * hq * ns;
+  dp.part_o = static_cast<float*>(workspace);
+  dp.part_ml = workspace != nullptr ? static_cast<float*>(workspace) + slots * head_dim : nullptr;
+  dp.n_seq = n_seq; dp.max_len = max_len; dp.hq = hq; dp.hkv = hkv; dp.head_dim = head_dim;
+  dp.n_layers = n_layers; dp.layer = layer; dp.mask_blocks = mask_blocks;
+  dp.block_size = p.block_size; dp.nsplit = ns; dp.scale = softmax_scale;
+  dp.cache_rows = max_len; dp.compact = 0; dp.route_heads = route_heads;
+  dp.sink_blocks = p.sink_blocks; dp.local_blocks = p.local_blocks;
+  return from_hip(flux::launch_decode(dp, static_cast<hipStream_t>(stream)));
+}
+
+// Checks shared by the two cache writers; on success *rows is the cache's
+// rows per (sequence, kv head).
+flux_status check_cache(int32_t hkv, int32_t head_dim, int32_t max_len, int32_t compact,
+                        flux_sa_params p, int32_t* rows) {
+  if (hkv < 1 || max_len < 1 || (compact != 0 && compact != 1)) return FLUX_ERR_INVALID_ARG;
+  if (!head_dim_supported(head_dim)) return FLUX_ERR_UNSUPPORTED;
+  if (compact) {
+    if (!sa_params_ok(p)) return FLUX_ERR_INVALID_ARG;
+    if (!block_supported(p.block_size)) return FLUX_ERR_UNSUPPORTED;
+    const int64_t r = flux::compact_rows(p.block_size, p.sink_blocks, p.local_blocks);
+    if (r > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
+    *rows = static_cast<int32_t>(r);
+  } else {
+    *rows = max_len;
+  }
+  return FLUX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -113,27 +194,21 @@ flux_status flux_attn_prefill(const uint16_t* q, const uint16_t* k, const uint16
                               int32_t layer, const int32_t* mask_row_ptr,
                               const int32_t* mask_col_idx, int32_t mask_blocks, flux_sa_params p,
                               void* stream) {
-  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || cu_seqlens == nullptr)
-    return FLUX_ERR_INVALID_ARG;
-  if (out == q || out == k || out == v) return FLUX_ERR_INVALID_ARG;
-  if (n_req < 1 || max_seqlen < 1) return FLUX_ERR_INVALID_ARG;
-  const flux_status st = check_attn_common(hq, hkv, head_dim, softmax_scale, route, n_layers, layer,
-                                           mask_row_ptr, mask_col_idx, mask_blocks, max_seqlen, p);
-  if (st != FLUX_OK) return st;
-  const int64_t n_qt = (static_cast<int64_t>(max_seqlen) + p.block_size - 1) / p.block_size;
-  if (n_qt * hq * n_req > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
-  // K/V rows of one request are addressed with 32-bit byte offsets
-  if (static_cast<int64_t>(max_seqlen) * hkv * head_dim * 2 > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
-  flux::PrefillParams pp{};
-  pp.q = q; pp.k = k; pp.v = v; pp.out = out;
-  pp.cu_seqlens = cu_seqlens; pp.route = route;
-  pp.row_ptr = mask_row_ptr; pp.col_idx = mask_col_idx;
-  pp.n_req = n_req; pp.max_seqlen = max_seqlen; pp.hq = hq; pp.hkv = hkv;
-  pp.head_dim = head_dim; pp.n_layers = n_layers; pp.layer = layer;
-  pp.mask_blocks = mask_blocks; pp.block_size = p.block_size;
-  pp.sink_blocks = p.sink_blocks; pp.local_blocks = p.local_blocks;
-  pp.scale = softmax_scale;
-  return from_hip(flux::launch_prefill(pp, static_cast<hipStream_t>(stream)));
+  return attn_prefill(q, k, v, out, cu_seqlens, n_req, max_seqlen, hq, hkv, head_dim,
+                      softmax_scale, route, n_layers, layer, mask_row_ptr, mask_col_idx,
+                      mask_blocks, p, 1, stream);
+}
+
+flux_status flux_attn_prefill_heads(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                    uint16_t* out, const int32_t* cu_seqlens, int32_t n_req,
+                                    int32_t max_seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
+                                    float softmax_scale, const uint8_t* route, int32_t n_layers,
+                                    int32_t layer, const int32_t* mask_row_ptr,
+                                    const int32_t* mask_col_idx, int32_t mask_blocks,
+                                    flux_sa_params p, void* stream) {
+  return attn_prefill(q, k, v, out, cu_seqlens, n_req, max_seqlen, hq, hkv, head_dim,
+                      softmax_scale, route, n_layers, layer, mask_row_ptr, mask_col_idx,
+                      mask_blocks, p, hkv, stream);
 }
 
 size_t flux_attn_decode_workspace_size(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_dim,
@@ -151,30 +226,22 @@ flux_status flux_attn_decode(const uint16_t* q, const uint16_t* k_cache, const u
                              int32_t layer, const int32_t* mask_row_ptr,
                              const int32_t* mask_col_idx, int32_t mask_blocks, flux_sa_params p,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr ||
-      seqlens == nullptr)
-    return FLUX_ERR_INVALID_ARG;
-  if (out == q) return FLUX_ERR_INVALID_ARG;
-  if (n_seq < 1 || max_len < 1) return FLUX_ERR_INVALID_ARG;
-  const flux_status st = check_attn_common(hq, hkv, head_dim, softmax_scale, route, n_layers, layer,
-                                           mask_row_ptr, mask_col_idx, mask_blocks, max_len, p);
-  if (st != FLUX_OK) return st;
-  const int32_t ns = flux::decode_splits(n_seq, hkv, max_len);
-  if (static_cast<int64_t>(n_seq) * hkv * ns > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
-  const size_t need = flux_attn_decode_workspace_size(n_seq, hq, hkv, head_dim, max_len);
-  if (ns > 1 && (workspace == nullptr || workspace_bytes < need)) return FLUX_ERR_WORKSPACE;
-  flux::DecodeParams dp{};
-  dp.q = q; dp.k_cache = k_cache; dp.v_cache = v_cache; dp.out = out;
-  dp.seqlens = seqlens; dp.route = route; dp.row_ptr = mask_row_ptr; dp.col_idx = mask_col_idx;
-  const size_t slots = static_cast<size_t>(n_seq) * hq * ns;
-  dp.part_o = static_cast<float*>(workspace);
-  dp.part_ml = workspace != nullptr ? static_cast<float*>(workspace) + slots * head_dim : nullptr;
-  dp.n_seq = n_seq; dp.max_len = max_len; dp.hq = hq; dp.hkv = hkv; dp.head_dim = head_dim;
-  dp.n_layers = n_layers; dp.layer = layer; dp.mask_blocks = mask_blocks;
-  dp.block_size = p.block_size; dp.nsplit = ns; dp.scale = softmax_scale;
-  dp.cache_rows = max_len; dp.compact = 0;
-  dp.sink_blocks = p.sink_blocks; dp.local_blocks = p.local_blocks;
-  return from_hip(flux::launch_decode(dp, static_cast<hipStream_t>(stream)));
+  return attn_decode(q, k_cache, v_cache, out, seqlens, n_seq, max_len, hq, hkv, head_dim,
+                     softmax_scale, route, n_layers, layer, mask_row_ptr, mask_col_idx,
+                     mask_blocks, p, 1, workspace, workspace_bytes, stream);
+}
+
+flux_status flux_attn_decode_heads(const uint16_t* q, const uint16_t* k_cache,
+                                   const uint16_t* v_cache, uint16_t* out, const int32_t* seqlens,
+                                   int32_t n_seq, int32_t max_len, int32_t hq, int32_t hkv,
+                                   int32_t head_dim, float softmax_scale, const uint8_t* route,
+                                   int32_t n_layers, int32_t layer, const int32_t* mask_row_ptr,
+                                   const int32_t* mask_col_idx, int32_t mask_blocks,
+                                   flux_sa_params p, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return attn_decode(q, k_cache, v_cache, out, seqlens, n_seq, max_len, hq, hkv, head_dim,
+                     softmax_scale, route, n_layers, layer, mask_row_ptr, mask_col_idx,
+                     mask_blocks, p, hkv, workspace, workspace_bytes, stream);
 }
 
 int64_t flux_kv_rows(int32_t max_len, flux_sa_params p, int32_t compact) {
@@ -183,26 +250,6 @@ int64_t flux_kv_rows(int32_t max_len, flux_sa_params p, int32_t compact) {
   if (!sa_params_ok(p) || p.block_size < 1) return FLUX_ERR_INVALID_ARG;
   return flux::compact_rows(p.block_size, p.sink_blocks, p.local_blocks);
 }
-
-namespace {
-// Checks shared by the two cache writers; on success *rows is the cache's
-// rows per (sequence, kv head).
-flux_status check_cache(int32_t hkv, int32_t head_dim, int32_t max_len, int32_t compact,
-                        flux_sa_params p, int32_t* rows) {
-  if (hkv < 1 || max_len < 1 || (compact != 0 && compact != 1)) return FLUX_ERR_INVALID_ARG;
-  if (!head_dim_supported(head_dim)) return FLUX_ERR_UNSUPPORTED;
-  if (compact) {
-    if (!sa_params_ok(p)) return FLUX_ERR_INVALID_ARG;
-    if (!block_supported(p.block_size)) return FLUX_ERR_UNSUPPORTED;
-    const int64_t r = flux::compact_rows(p.block_size, p.sink_blocks, p.local_blocks);
-    if (r > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
-    *rows = static_cast<int32_t>(r);
-  } else {
-    *rows = max_len;
-  }
-  return FLUX_OK;
-}
-}  // namespace
 
 flux_status flux_kv_store_prefill(const uint16_t* k, const uint16_t* v, const int32_t* cu_seqlens,
                                   int32_t n_req, int32_t max_seqlen, int32_t hkv, int32_t head_dim,
@@ -273,7 +320,7 @@ flux_status flux_attn_decode_sa_compact(const uint16_t* q, const uint16_t* k_cac
   dp.n_seq = n_seq; dp.max_len = max_len; dp.hq = hq; dp.hkv = hkv; dp.head_dim = head_dim;
   dp.n_layers = 1; dp.layer = 0; dp.mask_blocks = mask_blocks;
   dp.block_size = p.block_size; dp.nsplit = ns; dp.scale = softmax_scale;
-  dp.cache_rows = rows; dp.compact = 1;
+  dp.cache_rows = rows; dp.compact = 1; dp.route_heads = 1;
   dp.sink_blocks = p.sink_blocks; dp.local_blocks = p.local_blocks;
   return from_hip(flux::launch_decode(dp, static_cast<hipStream_t>(stream)));
 }

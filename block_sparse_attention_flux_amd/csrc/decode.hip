@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   const int N = min(max(p.seqlens[b], 1), p.max_len);
   // a compact cache only holds an SA layer's rows (and comes without a route)
   bool fa = false;
-  if (!p.compact) fa = p.route[static_cast<int64_t>(b) * p.n_layers + p.layer] != 0;
+  if (!p.compact) fa = p.route[route_index(b, p.n_layers, p.layer, p.route_heads, g)] != 0;
   const int B = p.block_size;
   const int mrow = min((N - 1) / B, p.mask_blocks - 1);
   int rp0 = 0, U;

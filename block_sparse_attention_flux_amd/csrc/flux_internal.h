@@ -18,6 +18,7 @@ struct PrefillParams {
   const int32_t* col_idx;
   int32_t n_req, max_seqlen, hq, hkv, head_dim, n_layers, layer, mask_blocks;
   int32_t block_size, sink_blocks, local_blocks;
+  int32_t route_heads;  // route decisions per (request, layer): 1, or hkv (one per kv head)
   float scale;
 };
 
@@ -34,11 +35,19 @@ struct DecodeParams {
   float* part_ml;  // [n_seq][hq][nsplit][2]
   int32_t n_seq, max_len, hq, hkv, head_dim, n_layers, layer, mask_blocks;
   int32_t block_size, nsplit;
+  int32_t route_heads;                // route decisions per (sequence, layer): 1 or hkv
   int32_t cache_rows;                 // rows per (sequence, kv head) in the caches
   int32_t compact;                    // 1: SA cache of sink rows + a ring of window rows
   int32_t sink_blocks, local_blocks;  // the SA pattern (compact row mapping)
   float scale;
 };
+
+// Route entry of (request r, layer, kv head g): route[r][layer] when one
+// decision covers the layer, route[r][layer][g] when each kv head has its own.
+__host__ __device__ inline int64_t route_index(int32_t r, int32_t n_layers, int32_t layer,
+                                               int32_t route_heads, int32_t g) {
+  return (static_cast<int64_t>(r) * n_layers + layer) * route_heads + (route_heads > 1 ? g : 0);
+}
 
 // Rows per (sequence, kv head) of a compact SA cache: sink + window blocks.
 inline int64_t compact_rows(int32_t block_size, int32_t sink_blocks, int32_t local_blocks) {

@@ -375,12 +375,29 @@ struct TileList {
   }
 };
 
-// Workgroup -> (kv group, query block heaviest first, request, head slot),
-// XCD-major so that consecutive work items share an XCD's L2.
-__device__ __forceinline__ void decode_work(int n_slots, int n_req, int n_qt, int& slot, int& req,
-                                            int& t, int& g) {
+// Workgroup -> (kv group, query block heaviest first, request, head slot).
+// Workgroup ids are dealt to the 8 XCDs round-robin (id % 8).  With one route
+// decision per layer the order is XCD-major: each XCD works through whole KV
+// head groups, so consecutive work items share an XCD's L2.  With one
+// decision per kv head that would leave the XCDs that drew FA groups running
+// long after the others, so there each XCD's share cycles through all kv
+// groups instead (heaviest query blocks still first).
+__device__ __forceinline__ void decode_work(int n_slots, int n_req, int n_qt, int hkv, bool by_head,
+                                            int& slot, int& req, int& t, int& g) {
   const int G = gridDim.x, bid = blockIdx.x;
-  int w = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  int w;
+  if (by_head && G % (8 * hkv) == 0) {
+    const int i = bid / 8;
+    g = i % hkv;
+    w = (i / hkv) * 8 + bid % 8;  // the other indices, heaviest blocks first
+    slot = w % n_slots;
+    w /= n_slots;
+    req = w % n_req;
+    w /= n_req;
+    t = n_qt - 1 - w;
+    return;
+  }
+  w = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
   slot = w % n_slots;
   w /= n_slots;
   req = w % n_req;
@@ -411,14 +428,14 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   const int group = p.hq / p.hkv;
   const int n_qt = (p.max_seqlen + BM - 1) / BM;
   int hi, req, t, g;
-  decode_work(group, p.n_req, n_qt, hi, req, t, g);
+  decode_work(group, p.n_req, n_qt, p.hkv, p.route_heads > 1, hi, req, t, g);
   const int head = g * group + hi;
 
   const int tok0 = p.cu_seqlens[req];
   const int S = p.cu_seqlens[req + 1] - tok0;
   const int q0 = t * BM;
   if (q0 >= S) return;
-  const bool fa = p.route[static_cast<int64_t>(req) * p.n_layers + p.layer] != 0;
+  const bool fa = p.route[route_index(req, p.n_layers, p.layer, p.route_heads, g)] != 0;
 
   __shared__ int32_t cols_raw[TileList<BM, BN>::kLdsCols];
   TileList<BM, BN> tiles;

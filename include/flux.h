@@ -144,6 +144,23 @@ flux_status flux_attn_prefill(const uint16_t* q, const uint16_t* k, const uint16
                               const int32_t* mask_col_idx, int32_t mask_blocks,
                               flux_sa_params p, void* stream);
 
+/*
+ * flux_attn_prefill_heads -- flux_attn_prefill with one route decision per
+ * (request, layer, kv head): route is uint8 [n_req][n_layers][hkv] and query
+ * head h follows route[r][layer][h / (hq / hkv)].  Head-level routing is the
+ * granularity the pages argue against on GPUs (load imbalance and
+ * synchronisation long tails between heads; technical summary, sections 1
+ * and 2); it is provided to measure that claim.  Everything else as
+ * flux_attn_prefill.
+ */
+flux_status flux_attn_prefill_heads(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                    uint16_t* out, const int32_t* cu_seqlens, int32_t n_req,
+                                    int32_t max_seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
+                                    float softmax_scale, const uint8_t* route, int32_t n_layers,
+                                    int32_t layer, const int32_t* mask_row_ptr,
+                                    const int32_t* mask_col_idx, int32_t mask_blocks,
+                                    flux_sa_params p, void* stream);
+
 /* Workspace bytes flux_attn_decode needs for these sizes [host] (0 on invalid
  * input). */
 size_t flux_attn_decode_workspace_size(int32_t n_seq, int32_t hq, int32_t hkv,
@@ -177,6 +194,17 @@ flux_status flux_attn_decode(const uint16_t* q, const uint16_t* k_cache,
                              const int32_t* mask_col_idx, int32_t mask_blocks,
                              flux_sa_params p, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/* flux_attn_decode_heads -- flux_attn_decode with route uint8
+ * [n_seq][n_layers][hkv], one decision per kv head (see flux_attn_prefill_heads). */
+flux_status flux_attn_decode_heads(const uint16_t* q, const uint16_t* k_cache,
+                                   const uint16_t* v_cache, uint16_t* out, const int32_t* seqlens,
+                                   int32_t n_seq, int32_t max_len, int32_t hq, int32_t hkv,
+                                   int32_t head_dim, float softmax_scale, const uint8_t* route,
+                                   int32_t n_layers, int32_t layer, const int32_t* mask_row_ptr,
+                                   const int32_t* mask_col_idx, int32_t mask_blocks,
+                                   flux_sa_params p, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /*
  * K/V caches for decode, and the compact SA-layer cache.

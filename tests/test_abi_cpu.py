@@ -31,7 +31,7 @@ def declared_symbols(header=HEADER):
 
 def test_exports_every_declared_symbol():
     syms = declared_symbols()
-    assert len(syms) == 13, syms
+    assert len(syms) == 15, syms
     raw = ctypes.CDLL(LIB)
     for s in syms:
         assert hasattr(raw, s), s
