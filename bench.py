@@ -212,6 +212,8 @@ def main():
     }
     result["head_routing"] = head_routing(flux, q, k, v, cu, S, row_ptr, col_idx, sa, fa_ms, sa_ms,
                                           fa_flops + sa_flops, stream, log)
+    result["soft_routing"] = soft_routing(flux, q, k, v, cu, S, row_ptr, col_idx, sa, fa_ms, sa_ms,
+                                          fa_flops, sa_flops, stream, log)
     att = attainable(flux, dev, stream, log)
     result["attainable"] = att
     result["roofline"]["frac_attainable"] = round(pre_tflops / att["mfma_tflops"], 4)
@@ -282,6 +284,31 @@ def head_routing(flux, q, k, v, cu, S, row_ptr, col_idx, sa, fa_ms, sa_ms, pair_
                    "keeps whole groups on one XCD for L2 locality; the same interleaving costs a "
                    "layer-routed FA layer ~4 % and an SA layer ~15 %)")
     return res
+
+
+def soft_routing(flux, q, k, v, cu, S, row_ptr, col_idx, sa, fa_ms, sa_ms, fa_flops, sa_flops, stream,
+                 log):
+    """The soft-routed forward r FA + (1 - r) SA of one 32K layer in one pass,
+    against the FA and SA layers run separately (the soft pass shares S and the
+    K/V tiles of the SA blocks with the FA branch)."""
+    import torch
+
+    r = torch.tensor([[0.5, 0.5]], dtype=torch.float32, device=q.device)
+    out = torch.empty_like(q)
+    flux.attn_prefill_soft(q, k, v, cu, S, r, 0, row_ptr, col_idx, sa, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record(stream)
+    for _ in range(reps):
+        flux.attn_prefill_soft(q, k, v, cu, S, r, 0, row_ptr, col_idx, sa, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    log(f"soft routing: one pass {ms:.3f} ms vs FA + SA layers {fa_ms + sa_ms:.3f} ms")
+    return {"soft_pass_ms": round(ms, 4), "fa_plus_sa_ms": round(fa_ms + sa_ms, 4),
+            "speedup_vs_two_layers": round((fa_ms + sa_ms) / ms, 3),
+            "tflops_fa_plus_sa_work": round((fa_flops + sa_flops) / ms / 1e9, 1)}
 
 
 def attainable(flux, dev, stream, log):

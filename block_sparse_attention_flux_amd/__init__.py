@@ -24,7 +24,7 @@ _LIB = _lib.load()
 
 __all__ = [
     "SAParams", "FluxError", "route", "route_workspace_size", "mask_blocks", "mask_nnz", "build_block_mask",
-    "attn_prefill", "decode_workspace_size", "decode_workspace", "attn_decode", "status_str",
+    "attn_prefill", "attn_prefill_soft", "decode_workspace_size", "decode_workspace", "attn_decode", "status_str",
     "kv_rows", "kv_cache", "kv_store_prefill", "kv_append", "attn_decode_sa_compact",
     "probe_mfma", "probe_read",
 ]
@@ -167,6 +167,29 @@ def attn_prefill(q, k, v, cu_seqlens, max_seqlen, route, layer, row_ptr, col_idx
         _ptr(row_ptr, torch.int32, "row_ptr"), _ptr(col_idx, torch.int32, "col_idx"),
         row_ptr.numel() - 1, sa.c(), _stream(q.device))
     _check(code, "flux_attn_prefill")
+    return out
+
+
+def attn_prefill_soft(q, k, v, cu_seqlens, max_seqlen, r_soft, layer, row_ptr, col_idx, sa,
+                      out=None, softmax_scale=None):
+    """Soft-routed forward r FA + (1 - r) SA of one layer (flux_attn_prefill_soft);
+    r_soft float32 [n_req][n_layers]."""
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (T, hkv, d) or v.shape != (T, hkv, d):
+        raise ValueError("k and v must be [T][hkv][head_dim] like q")
+    if out is None:
+        out = torch.empty_like(q)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    code = _LIB.flux_attn_prefill_soft(
+        _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"),
+        _ptr(out, torch.bfloat16, "out"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
+        cu_seqlens.numel() - 1, int(max_seqlen), hq, hkv, d, float(softmax_scale),
+        _ptr(r_soft, torch.float32, "r_soft"), r_soft.shape[1], int(layer),
+        _ptr(row_ptr, torch.int32, "row_ptr"), _ptr(col_idx, torch.int32, "col_idx"),
+        row_ptr.numel() - 1, sa.c(), _stream(q.device))
+    _check(code, "flux_attn_prefill_soft")
     return out
 
 

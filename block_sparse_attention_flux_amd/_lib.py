@@ -43,6 +43,8 @@ SIGNATURES = [
                               SAParamsC, _P, _S, _P]),
     ("flux_attn_prefill_heads", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P,
                                      _P, _I, SAParamsC, _P]),
+    ("flux_attn_prefill_soft", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P,
+                                    _P, _I, SAParamsC, _P]),
     ("flux_attn_decode_heads", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P, _P,
                                     _I, SAParamsC, _P, _S, _P]),
     ("flux_kv_rows", ctypes.c_int64, [_I, SAParamsC, _I]),

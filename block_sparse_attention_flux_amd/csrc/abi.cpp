@@ -49,7 +49,7 @@ flux_status attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          int32_t hkv, int32_t head_dim, float softmax_scale, const uint8_t* route,
                          int32_t n_layers, int32_t layer, const int32_t* mask_row_ptr,
                          const int32_t* mask_col_idx, int32_t mask_blocks, flux_sa_params p,
-                         int32_t route_heads, void* stream) {
+                         int32_t route_heads, const float* rsoft, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || cu_seqlens == nullptr)
     return FLUX_ERR_INVALID_ARG;
   if (out == q || out == k || out == v) return FLUX_ERR_INVALID_ARG;
@@ -71,6 +71,7 @@ flux_status attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
   pp.sink_blocks = p.sink_blocks; pp.local_blocks = p.local_blocks;
   pp.scale = softmax_scale;
   pp.route_heads = route_heads;
+  pp.rsoft = rsoft;
   return from_hip(flux::launch_prefill(pp, static_cast<hipStream_t>(stream)));
 }
 
@@ -196,7 +197,7 @@ flux_status flux_attn_prefill(const uint16_t* q, const uint16_t* k, const uint16
                               void* stream) {
   return attn_prefill(q, k, v, out, cu_seqlens, n_req, max_seqlen, hq, hkv, head_dim,
                       softmax_scale, route, n_layers, layer, mask_row_ptr, mask_col_idx,
-                      mask_blocks, p, 1, stream);
+                      mask_blocks, p, 1, nullptr, stream);
 }
 
 flux_status flux_attn_prefill_heads(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -208,7 +209,21 @@ flux_status flux_attn_prefill_heads(const uint16_t* q, const uint16_t* k, const 
                                     flux_sa_params p, void* stream) {
   return attn_prefill(q, k, v, out, cu_seqlens, n_req, max_seqlen, hq, hkv, head_dim,
                       softmax_scale, route, n_layers, layer, mask_row_ptr, mask_col_idx,
-                      mask_blocks, p, hkv, stream);
+                      mask_blocks, p, hkv, nullptr, stream);
+}
+
+flux_status flux_attn_prefill_soft(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   uint16_t* out, const int32_t* cu_seqlens, int32_t n_req,
+                                   int32_t max_seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
+                                   float softmax_scale, const float* r_soft, int32_t n_layers,
+                                   int32_t layer, const int32_t* mask_row_ptr,
+                                   const int32_t* mask_col_idx, int32_t mask_blocks,
+                                   flux_sa_params p, void* stream) {
+  if (r_soft == nullptr) return FLUX_ERR_INVALID_ARG;
+  // the weights take the route's place in the shared checks (the route itself is not read)
+  return attn_prefill(q, k, v, out, cu_seqlens, n_req, max_seqlen, hq, hkv, head_dim,
+                      softmax_scale, reinterpret_cast<const uint8_t*>(r_soft), n_layers, layer,
+                      mask_row_ptr, mask_col_idx, mask_blocks, p, 1, r_soft, stream);
 }
 
 size_t flux_attn_decode_workspace_size(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_dim,

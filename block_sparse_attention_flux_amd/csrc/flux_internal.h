@@ -19,6 +19,7 @@ struct PrefillParams {
   int32_t n_req, max_seqlen, hq, hkv, head_dim, n_layers, layer, mask_blocks;
   int32_t block_size, sink_blocks, local_blocks;
   int32_t route_heads;  // route decisions per (request, layer): 1, or hkv (one per kv head)
+  const float* rsoft;   // non-null: soft-routed forward, weight of FA per (request, layer)
   float scale;
 };
 

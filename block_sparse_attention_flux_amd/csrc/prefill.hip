@@ -151,8 +151,10 @@ struct TileLoader {
   }
 };
 
-// Per-wave state and math for 32 query rows of one head.
-template <int D, int BN>
+// Per-wave state and math for 32 query rows of one head.  NACC online-softmax
+// states (O, running max, running sum) share the wave's Q and S: one for
+// routed layers, two (FA and SA) for the soft-routed forward.
+template <int D, int BN, int NACC = 1>
 struct WaveAttn {
   static constexpr int KS = D / 16;   // k-steps of K Q^T
   static constexpr int DT = D / 32;   // 32-row tiles of O^T
@@ -162,8 +164,8 @@ struct WaveAttn {
   static constexpr int PK = BN / 4;   // packed bf16 pairs of P per lane
 
   bf16x8 qreg[KS];
-  f32x16 oacc[DT];
-  float m_run, l_run, cs;
+  f32x16 oacc[NACC][DT];
+  float m_run[NACC], l_run[NACC], cs;
   int row, wrow0, half, l32, vt_blk0, vt_in;
 
   __device__ __forceinline__ void init(const uint16_t* q, int tok0, int hq, int head, int q_row0,
@@ -181,10 +183,13 @@ struct WaveAttn {
       qreg[ks] = as_bf16x8(v);
     }
     cs = scale * kLog2e;  // scores -> log2 domain
-    m_run = kNegInf;
-    l_run = 0.0f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+    for (int a = 0; a < NACC; ++a) {
+      m_run[a] = kNegInf;
+      l_run[a] = 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[a][dt] = f32x16{};
+    }
     // V^T A operand (transpose read): source lane s = lane%16 points at key
     // 16ks + 8a + 4*half + s/4 and d = 32dt + 16*((lane/16)%2) + 4*(s%4), i.e.
     // block (4ks + 2a + half, 2dt + (lane/16)%2), byte (s/4)*32 + (s%4)*8
@@ -243,6 +248,7 @@ struct WaveAttn {
   // rows whose max grew past the slack move their reference (rescaling their
   // O and sum), and the exponentials are redone; rows that did not move get
   // bit-identical P, so each row's result depends on its own data only.
+  template <int A = 0>
   __device__ __forceinline__ void softmax(f32x16 (&sacc)[MT], int kst, uint32_t (&pk)[PK]) {
     if (kst + BN - 1 > wrow0) {  // tile crosses the diagonal: causal mask
 #pragma unroll
@@ -253,10 +259,10 @@ struct WaveAttn {
           if (key > row) sacc[mt][r] = kNegInf;
         }
     }
-    bool redo = m_run == kNegInf;
+    bool redo = m_run[A] == kNegInf;
     float ps = 0.0f;
     if (__ballot(redo) == 0) {
-      ps = exps(sacc, m_run, pk);
+      ps = exps(sacc, m_run[A], pk);
       redo = !(ps <= kSumLimit);
     }
     if (__ballot(redo) != 0) {
@@ -266,18 +272,18 @@ struct WaveAttn {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
       const float mxs = max_halves(mx) * cs;
-      const bool grow = mxs > m_run + kRescaleSlack;
+      const bool grow = mxs > m_run[A] + kRescaleSlack;
       if (__ballot(grow) != 0) {
-        const float m_new = grow ? mxs : m_run;
-        const float alpha = !grow ? 1.0f : (m_run == kNegInf) ? 0.0f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
+        const float m_new = grow ? mxs : m_run[A];
+        const float alpha = !grow ? 1.0f : (m_run[A] == kNegInf) ? 0.0f : fast_exp2(m_run[A] - m_new);
+        l_run[A] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-        m_run = m_new;
+        for (int dt = 0; dt < DT; ++dt) oacc[A][dt] *= alpha;
+        m_run[A] = m_new;
       }
-      ps = exps(sacc, m_run == kNegInf ? 0.0f : m_run, pk);
+      ps = exps(sacc, m_run[A] == kNegInf ? 0.0f : m_run[A], pk);
     }
-    l_run += ps;
+    l_run[A] += ps;
   }
 
   __device__ __forceinline__ s16x4 vt_read(const lds_u8* vl, int blk) const {
@@ -286,6 +292,7 @@ struct WaveAttn {
   }
 
   // O^T += V^T P^T for the V tile at vl
+  template <int A = 0>
   __device__ __forceinline__ void pv(const lds_u8* vl, const uint32_t (&pk)[PK]) {
     constexpr int PKS = BN / 16;  // k-steps of P V
     s16x8 vop[PKS][DT];
@@ -303,25 +310,34 @@ struct WaveAttn {
       const bf16x8 b = as_bf16x8(u32x4{pk[ks * 4], pk[ks * 4 + 1], pk[ks * 4 + 2], pk[ks * 4 + 3]});
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[ks][dt]), b,
-                                                           oacc[dt], 0, 0, 0);
+        oacc[A][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[ks][dt]), b,
+                                                              oacc[A][dt], 0, 0, 0);
     }
   }
 
-  // O = O^T / l, one query row per lane, 4 consecutive d per store
-  __device__ __forceinline__ void store(uint16_t* out, int tok0, int hq, int head, int S) const {
-    const float lt = sum_halves(l_run);
+  // O = w0 O_0 / l_0 (+ w1 O_1 / l_1), one query row per lane, 4 consecutive d per store
+  __device__ __forceinline__ void store(uint16_t* out, int tok0, int hq, int head, int S,
+                                        float w0 = 1.0f, float w1 = 0.0f) const {
+    float inv[NACC];
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) {
+      const float lt = sum_halves(l_run[a]);
+      inv[a] = (lt > 0.0f ? 1.0f / lt : 0.0f) * (a == 0 ? w0 : w1);
+    }
     if (row < S) {
-      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
       uint16_t* op = out + (static_cast<size_t>(tok0 + row) * hq + head) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] = oacc[0][dt][j * 4 + e] * inv[0];
+            if (NACC > 1) o[e] = __builtin_fmaf(oacc[NACC - 1][dt][j * 4 + e], inv[NACC - 1], o[e]);
+          }
           const int d0 = dt * 32 + j * 8 + half * 4;
-          const uint32_t lo = pack_bf16x2(oacc[dt][j * 4] * inv, oacc[dt][j * 4 + 1] * inv);
-          const uint32_t hi2 = pack_bf16x2(oacc[dt][j * 4 + 2] * inv, oacc[dt][j * 4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + d0) = u32x2{lo, hi2};
+          *reinterpret_cast<u32x2*>(op + d0) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         }
     }
   }
@@ -406,7 +422,11 @@ __device__ __forceinline__ void decode_work(int n_slots, int n_req, int n_qt, in
   g = w / n_qt;
 }
 
-template <int D, int BM, int BN, int OCC>
+// SOFT: the soft-routed forward, O = r FA + (1 - r) SA with r per (request,
+// layer): every tile up to the diagonal feeds the FA state, and the tiles of
+// the blocks in the query block's CSR row (a subset) also feed the SA state,
+// from the same S and the same K/V tiles in LDS.
+template <int D, int BM, int BN, int OCC, bool SOFT = false>
 __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParams p) {
   constexpr int NT = BM * 2;
   using Loader = TileLoader<D, NT, BN>;
@@ -435,14 +455,22 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   const int S = p.cu_seqlens[req + 1] - tok0;
   const int q0 = t * BM;
   if (q0 >= S) return;
-  const bool fa = p.route[route_index(req, p.n_layers, p.layer, p.route_heads, g)] != 0;
+  const bool fa = SOFT || p.route[route_index(req, p.n_layers, p.layer, p.route_heads, g)] != 0;
 
   __shared__ int32_t cols_raw[TileList<BM, BN>::kLdsCols];
   TileList<BM, BN> tiles;
   tiles.init(p, t, min(q0 + BM, S), fa, (lds_i32*)(cols_raw), tid, NT);
+  // SOFT: the SA blocks of this query block, walked in step with the FA tiles
+  TileList<BM, BN> sa_tiles;
+  int sa_next = 0, sa_blocks = 0;
+  if constexpr (SOFT) {
+    __syncthreads();  // the FA list has no LDS columns; the SA list stages its own
+    sa_tiles.init(p, t, min(q0 + BM, S), false, (lds_i32*)(cols_raw), tid, NT);
+    sa_blocks = (sa_tiles.n_tiles + TileList<BM, BN>::TPB - 1) / TileList<BM, BN>::TPB;
+  }
   Loader ld;
   ld.init(p.k, p.v, tok0, p.hkv, g, S, tid);
-  WaveAttn<D, BN> wa;
+  WaveAttn<D, BN, SOFT ? 2 : 1> wa;
   wa.init(p.q, tok0, p.hq, head, q0 + wave * 32, S, p.scale, lane);
   const int n_tiles = tiles.n_tiles;
   const int n_mine = tiles.visible(q0 + wave * 32, S);
@@ -459,12 +487,25 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
       ld.issue(false, kst_next, kn);
       ld.issue(true, kst_next, vn);
     }
+    bool in_sa = false;
+    if constexpr (SOFT) {  // is this tile's block the next block of the SA row?
+      const int blk = kst / BM;
+      while (sa_next < sa_blocks && sa_tiles.start(sa_next * TileList<BM, BN>::TPB) / BM < blk)
+        ++sa_next;
+      in_sa = sa_next < sa_blocks && sa_tiles.start(sa_next * TileList<BM, BN>::TPB) / BM == blk;
+    }
     if (n < n_mine) {
       f32x16 sacc[WaveAttn<D, BN>::MT];
       uint32_t pk[WaveAttn<D, BN>::PK];
       wa.qk(kc, sacc);
       wa.softmax(sacc, kst, pk);
       wa.pv(vc, pk);
+      if constexpr (SOFT) {
+        if (in_sa) {
+          wa.template softmax<1>(sacc, kst, pk);
+          wa.template pv<1>(vc, pk);
+        }
+      }
     }
     kst = kst_next;
     wait_vmem_all();
@@ -482,16 +523,23 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
       step(n + 1, k1, v1, k0, v0);
     }
   }
-  wa.store(p.out, tok0, p.hq, head, S);
+  if constexpr (SOFT) {
+    const float r = p.rsoft[static_cast<int64_t>(req) * p.n_layers + p.layer];
+    wa.store(p.out, tok0, p.hq, head, S, r, 1.0f - r);
+  } else {
+    wa.store(p.out, tok0, p.hq, head, S);
+  }
 }
 
 template <int D, int BM>
 hipError_t launch_typed(const PrefillParams& p, hipStream_t s) {
   const int n_qt = (p.max_seqlen + BM - 1) / BM;
-  const int group = p.hq / p.hkv;
-  (void)group;
   const int64_t grid = static_cast<int64_t>(n_qt) * p.hq * p.n_req;
-  prefill_kernel<D, BM, kBN, kOcc><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
+  if (p.rsoft != nullptr) {  // two O accumulators: built for 2 waves per SIMD
+    prefill_kernel<D, BM, kBN, 2, true><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
+  } else {
+    prefill_kernel<D, BM, kBN, kOcc><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 

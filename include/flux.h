@@ -161,6 +161,26 @@ flux_status flux_attn_prefill_heads(const uint16_t* q, const uint16_t* k, const 
                                     const int32_t* mask_col_idx, int32_t mask_blocks,
                                     flux_sa_params p, void* stream);
 
+/*
+ * flux_attn_prefill_soft -- the soft-routed forward of one layer:
+ *   out = r * FA(q, k, v) + (1 - r) * SA(q, k, v),  r = r_soft[req][layer],
+ * the convex combination of the two branches that the router's continuous
+ * weight forms during training (technical summary, section 2, differentiable
+ * soft routing).  One pass: every key tile up to the diagonal feeds the FA
+ * state, and the tiles of the mask's blocks (a subset) also feed a second,
+ * SA state from the same scores and the same K/V tiles.  Forward only.
+ * r_soft [device] fp32 [n_req][n_layers] (the caller's weights, e.g. a
+ * Gumbel-softmax sample or sigmoid(z); any value is combined as given).
+ * Everything else as flux_attn_prefill (no route: both branches are formed).
+ */
+flux_status flux_attn_prefill_soft(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   uint16_t* out, const int32_t* cu_seqlens, int32_t n_req,
+                                   int32_t max_seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
+                                   float softmax_scale, const float* r_soft, int32_t n_layers,
+                                   int32_t layer, const int32_t* mask_row_ptr,
+                                   const int32_t* mask_col_idx, int32_t mask_blocks,
+                                   flux_sa_params p, void* stream);
+
 /* Workspace bytes flux_attn_decode needs for these sizes [host] (0 on invalid
  * input). */
 size_t flux_attn_decode_workspace_size(int32_t n_seq, int32_t hq, int32_t hkv,

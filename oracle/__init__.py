@@ -19,7 +19,8 @@ What it computes, and where the pages define it
 * ``attention`` -- the plain masked-softmax definition
   ``O = softmax(Q K^T / sqrt(d) + mask) V`` with grouped KV heads, for prefill
   and for one-token decode that reuses the prefill route (technical summary,
-  section 2, deployment paragraph).
+  section 2, deployment paragraph); and the soft-routed forward
+  ``r FA + (1 - r) SA`` (technical summary, section 2, soft routing).
 
 Everything is float64, written for readability, not speed.  Inputs that the
 GPU sees as bf16 are widened exactly to float64 before they get here.
@@ -37,11 +38,12 @@ from .attention import (
     attention_prefill,
     attention_prefill_varlen,
     attention_decode,
+    attention_prefill_soft,
 )
 
 __all__ = [
     "pool_positions", "pool_mean", "router_mlp", "threshold_route", "route_requests",
     "num_blocks", "block_mask", "mask_to_csr", "mask_row_count", "mask_nnz",
     "allowed_matrix", "attention_probs", "attention_prefill",
-    "attention_prefill_varlen", "attention_decode",
+    "attention_prefill_varlen", "attention_decode", "attention_prefill_soft",
 ]

@@ -15,6 +15,10 @@ holds the token itself, so the query sits at position N-1 of N keys and uses
 the same rule (the route fixed at prefill is reused for decode: technical
 summary, section 2, deployment paragraph).
 
+Soft routing (training-time form; technical summary, section 2: the
+Gumbel-softmax relaxation forms a convex combination of the FA and SA branch
+with the router's continuous weight r):  O_soft = r * O_FA + (1 - r) * O_SA.
+
 The softmax is taken over a whole row at once (no online rescaling, no
 blocking); rows are only chunked to bound memory.
 """
@@ -134,3 +138,13 @@ def attention_decode(q, k_cache, v_cache, seqlens, fa, mask=None, block_size=Non
                                 block_size, scale)
             out[si, hi, :] = (p @ _as64(v_cache[b, g, :n, :]))[0]
     return out
+
+
+def attention_prefill_soft(q, k, v, r, mask, block_size, scale=None, rows=None, heads=None):
+    """Soft-routed prefill of one sequence: the convex combination
+    ``r * FA + (1 - r) * SA`` of the two branches, each the plain definition
+    above (technical summary, section 2, differentiable soft routing).
+    Returns float64 ``[len(rows)][len(heads)][d]``."""
+    fa = attention_prefill(q, k, v, True, mask, block_size, scale, rows, heads)
+    sa = attention_prefill(q, k, v, False, mask, block_size, scale, rows, heads)
+    return float(r) * fa + (1.0 - float(r)) * sa

@@ -314,3 +314,37 @@ def test_planted_mistakes_are_caught(monkeypatch):
         torch.from_numpy(q[40, 0][None, None]), torch.from_numpy(k[keys, 0][None]),
         torch.from_numpy(v[keys, 0][None]))[0, 0].numpy()
     assert not np.allclose(narrow[40, 0], ref, atol=1e-9)
+
+
+def _soft_reference(q, k, v, r, B, s, w, rows):
+    """r * causal SDPA + (1 - r) * SDPA over the gathered SA key set, by torch in float64."""
+    fa = sdpa_causal(q, k, v)
+    out = []
+    for p in rows:
+        keys = sa_key_set(p, B, s, w)
+        sa = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[p][:, None]), torch.from_numpy(k[keys].transpose(1, 0, 2)),
+            torch.from_numpy(v[keys].transpose(1, 0, 2)))[:, 0].numpy()
+        out.append(r * fa[p] + (1.0 - r) * sa)
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("r", [1.0, 0.0, 0.25])
+def test_soft_routing_is_the_convex_combination(r):
+    """The soft-routed forward (technical summary, section 2) against torch SDPA:
+    r = 1 is FA, r = 0 is SA, and in between the weights apply as r / 1 - r."""
+    S, B, s, w = 48, 8, 1, 2
+    q, k, v = rand_qkv(rng(31), S, 1, 1, 8)
+    rows = [0, 7, 8, 23, 24, 47]
+    m = oracle.block_mask(oracle.num_blocks(S, B), s, w)
+    got = oracle.attention_prefill_soft(q, k, v, r, m, B, rows=rows)[:, 0]
+    np.testing.assert_allclose(got, _soft_reference(q, k, v, r, B, s, w, rows)[:, 0], rtol=0, atol=1e-12)
+
+
+def test_soft_routing_planted_swap_is_caught():
+    S, B, s, w = 48, 8, 1, 2
+    q, k, v = rand_qkv(rng(31), S, 1, 1, 8)
+    rows = [23, 47]
+    m = oracle.block_mask(oracle.num_blocks(S, B), s, w)
+    swapped = oracle.attention_prefill_soft(q, k, v, 0.75, m, B, rows=rows)[:, 0]  # r and 1 - r exchanged
+    assert not np.allclose(swapped, _soft_reference(q, k, v, 0.25, B, s, w, rows)[:, 0], atol=1e-9)
