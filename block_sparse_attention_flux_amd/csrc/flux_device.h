@@ -45,9 +45,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // v_exp_f32: 2^x, exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value of lane (lane ^ 32), through the LDS crossbar (no LDS memory).
-__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
-
 // Both 32-lane halves of v after v_permlane32_swap: lo[l] = v[l % 32],
 // hi[l] = v[l % 32 + 32] (one VALU op, no LDS).
 __device__ __forceinline__ void halves(float v, float& lo, float& hi) {

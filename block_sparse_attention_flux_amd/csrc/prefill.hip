@@ -76,12 +76,6 @@ template <int CH>
 __device__ __forceinline__ int kslot(int row, int chunk) { return chunk ^ (row & (CH - 1)); }
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-// vmcnt(N): wait until at most N vector-memory operations of this wave are outstanding
-template <int N>
-__device__ __forceinline__ void wait_vmem_upto() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
 
 // Loads of one K or V tile into LDS by NT threads.  Load j of thread tid
 // fills LDS slot s = j*NT + tid (16 bytes, lane-linear per wave instruction);

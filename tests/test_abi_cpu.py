@@ -208,3 +208,28 @@ def test_compact_decode_validation():
     assert dec(p=SA(128, 1, 0), out=ctypes.c_void_p(0x2000)) == _lib.FLUX_ERR_INVALID_ARG
     assert dec(w=NULL, out=ctypes.c_void_p(0x2000)) == _lib.FLUX_ERR_WORKSPACE
     assert dec(wsb=ws - 4, out=ctypes.c_void_p(0x2000)) == _lib.FLUX_ERR_WORKSPACE
+
+
+def test_head_route_and_soft_validation():
+    """The per-kv-head and soft entry points reject bad arguments on the host
+    exactly like flux_attn_prefill / flux_attn_decode (nothing is launched)."""
+    sa = SA(128, 1, 16)
+    OUT = ctypes.c_void_p(0x2000)
+
+    def pre(fn, route=FAKE, hq=32, hkv=8, d=128, mb=256):
+        return fn(FAKE, FAKE, FAKE, OUT, FAKE, 1, 32768, hq, hkv, d, 0.088, route, 2, 0, FAKE, FAKE,
+                  mb, sa, NULL)
+    for fn in (lib.flux_attn_prefill_heads, lib.flux_attn_prefill_soft):
+        assert pre(fn, route=NULL) == _lib.FLUX_ERR_INVALID_ARG   # route / r_soft missing
+        assert pre(fn, hq=30) == _lib.FLUX_ERR_INVALID_ARG
+        assert pre(fn, d=96) == _lib.FLUX_ERR_UNSUPPORTED
+        assert pre(fn, hq=64, hkv=2) == _lib.FLUX_ERR_UNSUPPORTED  # group of 32 > 16
+        assert pre(fn, mb=255) == _lib.FLUX_ERR_INVALID_ARG
+    ws = lib.flux_attn_decode_workspace_size(16, 32, 8, 128, 32768)
+
+    def dec(route=FAKE, w=FAKE, wsb=ws):
+        return lib.flux_attn_decode_heads(FAKE, FAKE, FAKE, OUT, FAKE, 16, 32768, 32, 8, 128, 0.088, route,
+                                          2, 0, FAKE, FAKE, 256, sa, w, wsb, NULL)
+    assert dec(route=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(w=NULL) == _lib.FLUX_ERR_WORKSPACE
+    assert dec(wsb=ws - 1) == _lib.FLUX_ERR_WORKSPACE
