@@ -65,6 +65,26 @@ __device__ __forceinline__ float sum_halves(float v) {
   return lo + hi;
 }
 
+// The values of lanes l & ~16 and l | 16 (the two 16-lane rows of a 32-lane
+// half) after v_permlane16_swap, in both lanes (one VALU op, no LDS).
+__device__ __forceinline__ void quarters(float v, float& lo, float& hi) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  lo = u32_as_f32(r[0]);
+  hi = u32_as_f32(r[1]);
+}
+// max / sum of lanes l and l ^ 16, the same value (and bits) in both lanes
+__device__ __forceinline__ float max_quarters(float v) {
+  float lo, hi;
+  quarters(v, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float sum_quarters(float v) {
+  float lo, hi;
+  quarters(v, lo, hi);
+  return lo + hi;
+}
+
 // a.x + a.y + c for a packed bf16 pair a (v_dot2c_f32_bf16 against (1, 1))
 __device__ __forceinline__ float add_bf16_pair(uint32_t a, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),

@@ -66,43 +66,53 @@ typedef __attribute__((address_space(3))) int32_t lds_i32;
 
 // LDS layouts (64 banks of 4 bytes; a 16-byte read is served 16 lanes per
 // pass, an 8-byte read 32 lanes per pass):
-//   K tile: row-major, 16-byte chunk c of row r stored at chunk slot
-//           c ^ (r % CH): the 16 rows read by one pass of the K operand read
-//           land in 16 different slots, i.e. all 64 banks.
-//   V tile: 128-byte blocks of 4 keys x 16 d, block (key/4, d/16), inside a
-//           block key-major then d.  A transpose read of one 16-lane group
-//           covers exactly one block, and a 32-lane pass two adjacent blocks.
-template <int CH>
-__device__ __forceinline__ int kslot(int row, int chunk) { return chunk ^ (row & (CH - 1)); }
-
+//   K tile: row-major with rows CH + 1 slots of 16 bytes apart (one pad
+//           slot per row): the 16 rows read by one pass of the K operand read
+//           start 4 banks apart, i.e. cover all 64 banks, and a lane's reads
+//           for the k-steps are one base address plus constant offsets.
+//   V tile: 128-byte blocks of 4 keys x 16 d, inside a block key-major then
+//           d; block (quad q = key/4, d block j) stored at block index
+//           q * (D/16) + (j ^ (q & 1)).  A transpose read of one 16-lane group
+//           covers exactly one block, and the two groups of a 32-lane pass
+//           (quads 2i, 2i + 1, the same j) land 128 bytes apart modulo 256,
+//           i.e. on disjoint halves of the banks.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // Loads of one K or V tile into LDS by NT threads.  Load j of thread tid
 // fills LDS slot s = j*NT + tid (16 bytes, lane-linear per wave instruction);
 // the global chunk it fetches is chosen so that the slot ends up where the
-// layout wants it.  K: slot s is row s/CH, chunk slot s%CH.  V: slot s is
-// block s/8 = (key quad, d block), key 4*quad + (s%8)/2, chunk 2*dblk + s%2.
+// layout wants it.  K: slot s is row s/(CH+1), chunk s%(CH+1) (chunk CH is the
+// pad: its load is out of the buffer's range, so it fetches nothing and
+// writes zeros); the last K load covers only the first KSLOTS % NT threads.
+// V: slot s is stored block s/8 = (key quad, d block ^ (quad & 1)), key
+// 4*quad + (s%8)/2, chunk 2*dblk + s%2.
 template <int D, int NT, int BN>
 struct TileLoader {
   static constexpr int CH = D / 8;
-  static constexpr int TILEB = BN * D * 2;
+  static constexpr int KROW = CH + 1;                      // 16-byte slots per K row
+  static constexpr int KSLOTS = BN * KROW;
+  static constexpr int KTILEB = KSLOTS * 16;
+  static constexpr int KLOADS = (KSLOTS + NT - 1) / NT;
+  static constexpr int KLAST = KSLOTS - (KLOADS - 1) * NT;  // threads in the last K load
+  static constexpr int TILEB = BN * D * 2;                 // V tile
   static constexpr int LOADS = TILEB / (NT * 16);
   static_assert(TILEB % (NT * 16) == 0, "tile must split into whole wave loads");
+  static constexpr uint32_t kNoFetch = 0x80000000u;        // past any tile's buffer range
 
   const unsigned char* kbase;
   const unsigned char* vbase;
   uint32_t row_bytes;
   int S, tid, wave_u;
-  uint32_t koff[LOADS], voff[LOADS];
+  uint32_t koff[KLOADS], voff[LOADS];
 
-  __device__ __forceinline__ void k_src(int j, int& r, int& c) const {
+  __device__ __forceinline__ uint32_t k_src(int j) const {
     const int s = j * NT + tid;
-    r = s / CH;
-    c = kslot<CH>(s / CH, s % CH);
+    const int r = s / KROW, c = s % KROW;
+    return c == CH ? kNoFetch : r * row_bytes + c * 16;
   }
   __device__ __forceinline__ void v_src(int j, int& r, int& c) const {
     const int s = j * NT + tid;
-    const int blk = s / 8, kq = blk / (D / 16), dblk = blk % (D / 16);
+    const int blk = s / 8, kq = blk / (D / 16), dblk = (blk % (D / 16)) ^ (kq & 1);
     r = 4 * kq + (s % 8) / 2;
     c = 2 * dblk + (s % 2);
   }
@@ -118,10 +128,10 @@ struct TileLoader {
     tid = thread;
     wave_u = __builtin_amdgcn_readfirstlane(thread >> 6);
 #pragma unroll
+    for (int j = 0; j < KLOADS; ++j) koff[j] = k_src(j);
+#pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       int r, c;
-      k_src(j, r, c);
-      koff[j] = r * row_bytes + c * 16;
       v_src(j, r, c);
       voff[j] = r * row_bytes + c * 16;
     }
@@ -137,105 +147,141 @@ struct TileLoader {
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned char*>(base), 0, static_cast<int>(rows * row_bytes), kBufferFlags);
     lds_u8* dst0 = dst + wave_u * 64 * 16;
+    if (is_v) {
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, reinterpret_cast<lds_void*>(dst0 + j * NT * 16),
-                                               16, static_cast<int>(is_v ? voff[j] : koff[j]), 0, 0,
-                                               0);
+      for (int j = 0; j < LOADS; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, reinterpret_cast<lds_void*>(dst0 + j * NT * 16), 16,
+                                                 static_cast<int>(voff[j]), 0, 0, 0);
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < KLOADS - 1; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, reinterpret_cast<lds_void*>(dst0 + j * NT * 16), 16,
+                                               static_cast<int>(koff[j]), 0, 0, 0);
+    // last K load: only the threads whose slot is inside the tile (the LDS
+    // array ends at the tile; the other lanes must not write)
+    if (wave_u * 64 < KLAST && tid < KLAST)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc,
+                                               reinterpret_cast<lds_void*>(dst0 + (KLOADS - 1) * NT * 16),
+                                               16, static_cast<int>(koff[KLOADS - 1]), 0, 0, 0);
   }
 };
 
-// Per-wave state and math for 32 query rows of one head.  NACC online-softmax
-// states (O, running max, running sum) share the wave's Q and S: one for
-// routed layers, two (FA and SA) for the soft-routed forward.
+// Per-wave state and math for 32 query rows of one head, on 16x16x32 MFMA
+// tiles.  S^T = K Q^T is 2 key tiles x 2 row tiles of 16 x 16: lane l holds
+// rows l%16 and 16 + l%16 (row tile c), keys 16kt + 4(l/16) + r (r = 0..3),
+// so every row is spread over the 4 lanes l%16 + 16g.  O^T is D/16 d tiles x
+// 2 row tiles.  Every MFMA of a tile is independent of the other chains: 4
+// accumulators of K Q^T (4 dependent k-steps each for d 128), and each O^T
+// tile takes one 32-key k-step.  NACC online-softmax states (O, running max,
+// running sum) share the wave's Q and S: one for routed layers, two (FA and
+// SA) for the soft-routed forward.
+//
+// The k index of the P V product runs over the tile's 32 keys in the order
+// the S^T layout leaves them in a lane: k = 8g + e is key 16(e/4) + 4g + e%4,
+// for P (the B operand, straight from the exponentials) and for V^T (the A
+// operand, two transpose reads of 4 keys each) alike.
 template <int D, int BN, int NACC = 1>
 struct WaveAttn {
-  static constexpr int KS = D / 16;   // k-steps of K Q^T
-  static constexpr int DT = D / 32;   // 32-row tiles of O^T
-  static constexpr int CH = D / 8;
-  static constexpr int ROWB = D * 2;
-  static constexpr int MT = BN / 32;  // 32-key tiles of S^T
-  static constexpr int PK = BN / 4;   // packed bf16 pairs of P per lane
+  static_assert(BN == 32, "one 32-key k-step of P V per tile");
+  static constexpr int KS = D / 32;   // k-steps of K Q^T
+  static constexpr int DT = D / 16;   // 16-row d tiles of O^T
+  static constexpr int KROW = D / 8 + 1;
+  static constexpr int VBLK = D / 16;  // 128-byte V blocks per key quad
+  static constexpr int PK = 8;         // packed bf16 pairs of P per lane (2 rows x 4)
 
-  bf16x8 qreg[KS];
-  f32x16 oacc[NACC][DT];
-  float m_run[NACC], l_run[NACC], cs;
-  int row, wrow0, half, l32, vt_blk0, vt_in;
+  bf16x8 qreg[2][KS];
+  f32x4 oacc[NACC][2][DT];
+  float m_run[NACC][2], l_run[NACC][2], cs;
+  int l16, grp, wrow0, krd, vrd_e, vrd_o;
 
   __device__ __forceinline__ void init(const uint16_t* q, int tok0, int hq, int head, int q_row0,
                                        int S, float scale, int lane) {
-    l32 = lane & 31;
-    half = lane >> 5;
+    l16 = lane & 15;
+    grp = lane >> 4;
     wrow0 = q_row0;
-    row = q_row0 + l32;
-    const bool row_ok = row < S;
-    const uint16_t* qp =
-        q + (static_cast<size_t>(tok0 + (row_ok ? row : 0)) * hq + head) * D + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = row_ok ? ld16(qp + ks * 16) : u32x4{0, 0, 0, 0};
-      qreg[ks] = as_bf16x8(v);
+    for (int c = 0; c < 2; ++c) {
+      const int row = q_row0 + 16 * c + l16;
+      const bool row_ok = row < S;
+      const uint16_t* qp =
+          q + (static_cast<size_t>(tok0 + (row_ok ? row : 0)) * hq + head) * D + grp * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = row_ok ? ld16(qp + ks * 32) : u32x4{0, 0, 0, 0};
+        qreg[c][ks] = as_bf16x8(v);
+      }
     }
     cs = scale * kLog2e;  // scores -> log2 domain
 #pragma unroll
-    for (int a = 0; a < NACC; ++a) {
-      m_run[a] = kNegInf;
-      l_run[a] = 0.0f;
+    for (int a = 0; a < NACC; ++a)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[a][dt] = f32x16{};
-    }
-    // V^T A operand (transpose read): source lane s = lane%16 points at key
-    // 16ks + 8a + 4*half + s/4 and d = 32dt + 16*((lane/16)%2) + 4*(s%4), i.e.
-    // block (4ks + 2a + half, 2dt + (lane/16)%2), byte (s/4)*32 + (s%4)*8
-    vt_blk0 = half * (D / 16) + ((lane >> 4) & 1);
-    vt_in = ((lane & 15) >> 2) * 32 + (lane & 3) * 8;
-  }
-
-  // S^T for the 64 keys of the K tile at kl: A = key row mt*32 + l32, chunk 2ks + half
-  __device__ __forceinline__ void qk(const lds_u8* kl, f32x16 (&sacc)[MT]) const {
-    u32x4 kop[MT][KS];
+      for (int c = 0; c < 2; ++c) {
+        m_run[a][c] = kNegInf;
+        l_run[a][c] = 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int key = mt * 32 + l32;
-      const lds_u8* kp = kl + key * ROWB;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kop[mt][ks] = *reinterpret_cast<const lds_u32x4*>(kp + (kslot<CH>(key, 2 * ks + half) << 4));
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      sacc[mt] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[mt][ks]), qreg[ks], sacc[mt],
-                                                           0, 0, 0);
-    }
-  }
-
-  // P = 2^(S cs - mu) as packed bf16 pairs; returns this lane's sum of the
-  // same bf16 P that the P V product uses (two pairs per op).
-  __device__ __forceinline__ float exps(const f32x16 (&sacc)[MT], float mu, uint32_t (&pk)[PK]) const {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(sacc[mt][r], cs, -mu));
-        const float p1 = fast_exp2(__builtin_fmaf(sacc[mt][r + 1], cs, -mu));
-        pk[mt * 8 + r / 2] = pack_bf16x2(p0, p1);
+        for (int dt = 0; dt < DT; ++dt) oacc[a][c][dt] = f32x4{};
       }
-    float s0 = 0.0f, s1 = 0.0f;
+    // K operand: key row l%16 (+16 kt), chunk 4ks + g: one base, constant offsets
+    krd = (l16 * KROW + grp) * 16;
+    // V^T operand (transpose read): the 16 lanes of group g read the 128-byte
+    // block of key quad 4kt + g and d block dt, stored at block index
+    // quad * VBLK + (dt ^ (quad & 1)), byte 8 * (l%16).  g & 1 = quad & 1, so
+    // even dt sit at +128 g&1 and odd dt at -128 g&1 from the plain position.
+    const int h = grp & 1;
+    vrd_e = grp * VBLK * 128 + h * 128 + l16 * 8;
+    vrd_o = grp * VBLK * 128 - h * 128 + l16 * 8;
+  }
+
+  // S^T of the 32-key tile at kl
+  __device__ __forceinline__ void qk(const lds_u8* kl, f32x4 (&s)[2][2]) const {
+    u32x4 kop[2][KS];
 #pragma unroll
-    for (int i = 0; i < PK; i += 2) {
-      s0 = add_bf16_pair(pk[i], s0);
-      s1 = add_bf16_pair(pk[i + 1], s1);
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kop[kt][ks] = *reinterpret_cast<const lds_u32x4*>(kl + krd + (kt * 16 * KROW + 4 * ks) * 16);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) s[kt][c] = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          s[kt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[kt][ks]), qreg[c][ks], s[kt][c],
+                                                             0, 0, 0);
+  }
+
+  // P = 2^(S cs - mu) as packed bf16 pairs (pk[4c + j]: row tile c); ps[c] is
+  // this lane's sum of the same bf16 P that the P V product uses
+  __device__ __forceinline__ void exps(const f32x4 (&s)[2][2], const float (&mu)[2], uint32_t (&pk)[PK],
+                                       float (&ps)[2]) const {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[kt][c][r], cs, -mu[c]));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kt][c][r + 1], cs, -mu[c]));
+          pk[4 * c + 2 * kt + r / 2] = pack_bf16x2(p0, p1);
+        }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float a = add_bf16_pair(pk[4 * c], 0.0f);
+#pragma unroll
+      for (int j = 1; j < 4; ++j) a = add_bf16_pair(pk[4 * c + j], a);
+      ps[c] = a;
     }
-    return s0 + s1;
   }
 
   // Causal mask, exponentials against the running max, and the max update
   // only where it is needed.  The exponentials are taken first with the
   // current running max: as long as no P of this lane exceeds 2^16 (its
-  // partial row sum stays below kSumLimit) the tile is done, and the running
+  // partial row sums stay below kSumLimit) the tile is done, and the running
   // max is left as it is (any P up to 2^16 is exact in fp32/bf16 range terms
   // and the final division uses the same reference).  Otherwise (and on the
   // first tile, when there is no reference yet) the tile's row max is taken,
@@ -243,96 +289,107 @@ struct WaveAttn {
   // O and sum), and the exponentials are redone; rows that did not move get
   // bit-identical P, so each row's result depends on its own data only.
   template <int A = 0>
-  __device__ __forceinline__ void softmax(f32x16 (&sacc)[MT], int kst, uint32_t (&pk)[PK]) {
+  __device__ __forceinline__ void softmax(f32x4 (&s)[2][2], int kst, uint32_t (&pk)[PK]) {
     if (kst + BN - 1 > wrow0) {  // tile crosses the diagonal: causal mask
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kst + mt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          if (key > row) sacc[mt][r] = kNegInf;
-        }
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kst + 16 * kt + 4 * grp + r;
+            if (key > wrow0 + 16 * c + l16) s[kt][c][r] = kNegInf;
+          }
     }
-    bool redo = m_run[A] == kNegInf;
-    float ps = 0.0f;
-    if (__ballot(redo) == 0) {
-      ps = exps(sacc, m_run[A], pk);
-      redo = !(ps <= kSumLimit);
+    float ps[2] = {0.0f, 0.0f};
+    bool slow = __ballot(m_run[A][0] == kNegInf || m_run[A][1] == kNegInf) != 0;  // wave-uniform
+    if (!slow) {
+      exps(s, m_run[A], pk, ps);
+      slow = __ballot(!(ps[0] + ps[1] <= kSumLimit)) != 0;
     }
-    if (__ballot(redo) != 0) {
-      float mx = kNegInf;
+    if (slow) {
+      bool grow[2];
+      float mxs[2];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int c = 0; c < 2; ++c) {
+        float mx = kNegInf;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
-      const float mxs = max_halves(mx) * cs;
-      const bool grow = mxs > m_run[A] + kRescaleSlack;
-      if (__ballot(grow) != 0) {
-        const float m_new = grow ? mxs : m_run[A];
-        const float alpha = !grow ? 1.0f : (m_run[A] == kNegInf) ? 0.0f : fast_exp2(m_run[A] - m_new);
-        l_run[A] *= alpha;
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[A][dt] *= alpha;
-        m_run[A] = m_new;
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kt][c][r]);
+        mxs[c] = max_quarters(max_halves(mx)) * cs;
+        grow[c] = mxs[c] > m_run[A][c] + kRescaleSlack;
       }
-      ps = exps(sacc, m_run[A] == kNegInf ? 0.0f : m_run[A], pk);
+      if (__ballot(grow[0] || grow[1]) != 0) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float m_new = grow[c] ? mxs[c] : m_run[A][c];
+          const float alpha =
+              !grow[c] ? 1.0f : (m_run[A][c] == kNegInf) ? 0.0f : fast_exp2(m_run[A][c] - m_new);
+          l_run[A][c] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[A][c][dt] *= alpha;
+          m_run[A][c] = m_new;
+        }
+      }
+      const float mu[2] = {m_run[A][0] == kNegInf ? 0.0f : m_run[A][0],
+                           m_run[A][1] == kNegInf ? 0.0f : m_run[A][1]};
+      exps(s, mu, pk, ps);
     }
-    l_run[A] += ps;
+    l_run[A][0] += ps[0];
+    l_run[A][1] += ps[1];
   }
 
-  __device__ __forceinline__ s16x4 vt_read(const lds_u8* vl, int blk) const {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        reinterpret_cast<lds_s16x4*>(const_cast<lds_u8*>(vl) + blk * 128 + vt_in));
+  // 4 keys (quad 4kt + g) x 16 d (tile dt) of V^T, transposed: element e of
+  // lane l is V[16kt + 4g + e][16dt + l%16]
+  __device__ __forceinline__ s16x4 vt_read(const lds_u8* vl, int kt, int dt) const {
+    const int off = ((dt & 1) ? vrd_o : vrd_e) + (kt * 4 * VBLK + dt) * 128;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(const_cast<lds_u8*>(vl) + off));
   }
 
   // O^T += V^T P^T for the V tile at vl
   template <int A = 0>
   __device__ __forceinline__ void pv(const lds_u8* vl, const uint32_t (&pk)[PK]) {
-    constexpr int PKS = BN / 16;  // k-steps of P V
-    s16x8 vop[PKS][DT];
+    s16x8 vop[DT];
 #pragma unroll
-    for (int ks = 0; ks < PKS; ++ks)
+    for (int dt = 0; dt < DT; ++dt)
+      vop[dt] = __builtin_shufflevector(vt_read(vl, 0, dt), vt_read(vl, 1, dt), 0, 1, 2, 3, 4, 5, 6, 7);
+    bf16x8 b[2];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int blk = vt_blk0 + 4 * ks * (D / 16) + 2 * dt;
-        const s16x4 lo = vt_read(vl, blk);                  // keys 16ks + 4*half + m
-        const s16x4 hi4 = vt_read(vl, blk + 2 * (D / 16));  // keys 16ks + 8 + 4*half + m
-        vop[ks][dt] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+    for (int c = 0; c < 2; ++c) b[c] = as_bf16x8(u32x4{pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]});
 #pragma unroll
-    for (int ks = 0; ks < PKS; ++ks) {
-      const bf16x8 b = as_bf16x8(u32x4{pk[ks * 4], pk[ks * 4 + 1], pk[ks * 4 + 2], pk[ks * 4 + 3]});
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        oacc[A][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[ks][dt]), b,
-                                                              oacc[A][dt], 0, 0, 0);
-    }
+      for (int c = 0; c < 2; ++c)
+        oacc[A][c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[dt]), b[c],
+                                                                 oacc[A][c][dt], 0, 0, 0);
   }
 
-  // O = w0 O_0 / l_0 (+ w1 O_1 / l_1), one query row per lane, 4 consecutive d per store
+  // O = w0 O_0 / l_0 (+ w1 O_1 / l_1); lane l writes d 16dt + 4(l/16) .. +3 of its two rows
   __device__ __forceinline__ void store(uint16_t* out, int tok0, int hq, int head, int S,
                                         float w0 = 1.0f, float w1 = 0.0f) const {
-    float inv[NACC];
 #pragma unroll
-    for (int a = 0; a < NACC; ++a) {
-      const float lt = sum_halves(l_run[a]);
-      inv[a] = (lt > 0.0f ? 1.0f / lt : 0.0f) * (a == 0 ? w0 : w1);
-    }
-    if (row < S) {
-      uint16_t* op = out + (static_cast<size_t>(tok0 + row) * hq + head) * D;
+    for (int c = 0; c < 2; ++c) {
+      float inv[NACC];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int a = 0; a < NACC; ++a) {
+        const float lt = sum_quarters(sum_halves(l_run[a][c]));
+        inv[a] = (lt > 0.0f ? 1.0f / lt : 0.0f) * (a == 0 ? w0 : w1);
+      }
+      const int row = wrow0 + 16 * c + l16;
+      if (row < S) {
+        uint16_t* op = out + (static_cast<size_t>(tok0 + row) * hq + head) * D + 4 * grp;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int dt = 0; dt < DT; ++dt) {
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            o[e] = oacc[0][dt][j * 4 + e] * inv[0];
-            if (NACC > 1) o[e] = __builtin_fmaf(oacc[NACC - 1][dt][j * 4 + e], inv[NACC - 1], o[e]);
+            o[e] = oacc[0][c][dt][e] * inv[0];
+            if (NACC > 1) o[e] = __builtin_fmaf(oacc[NACC - 1][c][dt][e], inv[NACC - 1], o[e]);
           }
-          const int d0 = dt * 32 + j * 8 + half * 4;
-          *reinterpret_cast<u32x2*>(op + d0) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          *reinterpret_cast<u32x2*>(op + 16 * dt) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         }
+      }
     }
   }
 };
@@ -424,12 +481,12 @@ template <int D, int BM, int BN, int OCC, bool SOFT = false>
 __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParams p) {
   constexpr int NT = BM * 2;
   using Loader = TileLoader<D, NT, BN>;
-  constexpr int TILEB = Loader::TILEB;
+  constexpr int TILEB = Loader::TILEB, KTILEB = Loader::KTILEB;
   // Four separate arrays: the compiler can then see that the LDS reads of
   // one buffer pair never alias the DMA still filling the other pair, and
   // does not make the reads wait for it.
-  __shared__ __attribute__((aligned(16))) unsigned char k0_raw[TILEB];
-  __shared__ __attribute__((aligned(16))) unsigned char k1_raw[TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char k0_raw[KTILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char k1_raw[KTILEB];
   __shared__ __attribute__((aligned(16))) unsigned char v0_raw[TILEB];
   __shared__ __attribute__((aligned(16))) unsigned char v1_raw[TILEB];
   lds_u8* const k0 = (lds_u8*)(k0_raw);  // the same arrays, addressed as LDS
@@ -489,7 +546,7 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
       in_sa = sa_next < sa_blocks && sa_tiles.start(sa_next * TileList<BM, BN>::TPB) / BM == blk;
     }
     if (n < n_mine) {
-      f32x16 sacc[WaveAttn<D, BN>::MT];
+      f32x4 sacc[2][2];
       uint32_t pk[WaveAttn<D, BN>::PK];
       wa.qk(kc, sacc);
       wa.softmax(sacc, kst, pk);
