@@ -64,12 +64,14 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 
-// LDS layouts (64 banks of 4 bytes; a 16-byte read is served 16 lanes per
-// pass, an 8-byte read 32 lanes per pass):
-//   K tile: row-major with rows CH + 1 slots of 16 bytes apart (one pad
-//           slot per row): the 16 rows read by one pass of the K operand read
-//           start 4 banks apart, i.e. cover all 64 banks, and a lane's reads
-//           for the k-steps are one base address plus constant offsets.
+// LDS layouts (64 banks of 4 bytes; an 8-byte read is served 32 lanes per
+// pass):
+//   K tile: row-major with rows CH + 2 slots of 16 bytes apart (two pad slots
+//           per row), so a lane's reads for the k-steps are one base address
+//           plus constant offsets.  For the K operand read (lane l: row l%16
+//           of a 16-key half, chunk 4ks + l/16) this stride measured free of
+//           bank conflicts on gfx950, where CH + 1 and CH + 3 cost 4 extra
+//           cycles per read (SQ_LDS_BANK_CONFLICT).
 //   V tile: 128-byte blocks of 4 keys x 16 d, inside a block key-major then
 //           d; block (quad q = key/4, d block j) stored at block index
 //           q * (D/16) + (j ^ (q & 1)).  A transpose read of one 16-lane group
@@ -81,15 +83,16 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 // Loads of one K or V tile into LDS by NT threads.  Load j of thread tid
 // fills LDS slot s = j*NT + tid (16 bytes, lane-linear per wave instruction);
 // the global chunk it fetches is chosen so that the slot ends up where the
-// layout wants it.  K: slot s is row s/(CH+1), chunk s%(CH+1) (chunk CH is the
-// pad: its load is out of the buffer's range, so it fetches nothing and
-// writes zeros); the last K load covers only the first KSLOTS % NT threads.
+// layout wants it.  K: slot s is row s/KROW, chunk s%KROW (chunks CH and up
+// are the pad: their loads are out of the buffer's range, so they fetch
+// nothing and write zeros); the last K load covers only the first
+// KSLOTS % NT threads.
 // V: slot s is stored block s/8 = (key quad, d block ^ (quad & 1)), key
 // 4*quad + (s%8)/2, chunk 2*dblk + s%2.
 template <int D, int NT, int BN>
 struct TileLoader {
   static constexpr int CH = D / 8;
-  static constexpr int KROW = CH + 1;                      // 16-byte slots per K row
+  static constexpr int KROW = CH + 2;                      // 16-byte slots per K row
   static constexpr int KSLOTS = BN * KROW;
   static constexpr int KTILEB = KSLOTS * 16;
   static constexpr int KLOADS = (KSLOTS + NT - 1) / NT;
@@ -108,7 +111,7 @@ struct TileLoader {
   __device__ __forceinline__ uint32_t k_src(int j) const {
     const int s = j * NT + tid;
     const int r = s / KROW, c = s % KROW;
-    return c == CH ? kNoFetch : r * row_bytes + c * 16;
+    return c >= CH ? kNoFetch : r * row_bytes + c * 16;
   }
   __device__ __forceinline__ void v_src(int j, int& r, int& c) const {
     const int s = j * NT + tid;
@@ -186,7 +189,7 @@ struct WaveAttn {
   static_assert(BN == 32, "one 32-key k-step of P V per tile");
   static constexpr int KS = D / 32;   // k-steps of K Q^T
   static constexpr int DT = D / 16;   // 16-row d tiles of O^T
-  static constexpr int KROW = D / 8 + 1;
+  static constexpr int KROW = D / 8 + 2;
   static constexpr int VBLK = D / 16;  // 128-byte V blocks per key quad
   static constexpr int PK = 8;         // packed bf16 pairs of P per lane (2 rows x 4)
 
