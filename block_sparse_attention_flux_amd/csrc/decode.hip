@@ -66,18 +66,19 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   const int group = p.hq / p.hkv;
 
   const int N = min(max(p.seqlens[b], 1), p.max_len);
+  const int B = p.block_size;
+  const int mrow = min((N - 1) / B, p.mask_blocks - 1);
+  // The route, the mask row's bounds and its first 64 columns are read
+  // together, before the layer type is known (the mask is always present),
+  // so an SA layer's first K/V loads wait on one round trip, not three.
+  // Lane i keeps column i of the row.
+  const int rp0 = p.row_ptr[mrow];
+  const int n_blk = max(p.row_ptr[mrow + 1] - rp0, 0);
   // a compact cache only holds an SA layer's rows (and comes without a route)
   bool fa = false;
   if (!p.compact) fa = p.route[route_index(b, p.n_layers, p.layer, p.route_heads, g)] != 0;
-  const int B = p.block_size;
-  const int mrow = min((N - 1) / B, p.mask_blocks - 1);
-  int rp0 = 0, U;
-  if (fa) {
-    U = N;
-  } else {
-    rp0 = p.row_ptr[mrow];
-    U = max(p.row_ptr[mrow + 1] - rp0, 0) * B;
-  }
+  const int col_lane = lane < n_blk ? min(max(p.col_idx[rp0 + lane], 0), mrow) : 0;
+  const int U = fa ? N : n_blk * B;
   // contiguous range of visited-key indices for this split, chunk aligned
   const int per = ((U + p.nsplit - 1) / p.nsplit + kChunk - 1) / kChunk * kChunk;
   const int u0 = split * per;
@@ -87,10 +88,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   const uint16_t* kc = p.k_cache + (static_cast<size_t>(b) * p.hkv + g) * cache_head;
   const uint16_t* vc = p.v_cache + (static_cast<size_t>(b) * p.hkv + g) * cache_head;
 
-  // first key position of the chunk that starts at visited index u
+  // first key position of the chunk that starts at visited index u (wave-uniform)
   auto chunk_key = [&](int u) -> int {
     if (fa) return u;
-    const int blk = min(max(p.col_idx[rp0 + u / B], 0), mrow);
+    const int bi = u / B;
+    const int blk = bi < 64 ? __builtin_amdgcn_readlane(col_lane, bi) : min(max(p.col_idx[rp0 + bi], 0), mrow);
     return blk * B + u % B;
   };
   // cache row of key position k: the position itself in a full cache; in a
