@@ -16,6 +16,10 @@ What it computes, and where the pages define it
   a causal local window of blocks (the pages name block-sparse attention via
   the Block-Sparse-Attention library on the Qwen3-4B model card, "Sample
   Usage"; the sink+window pattern is a reading).
+* ``dynmask``   -- a content-aware block mask (mean-pooled coarse attention,
+  Top-tau selection); the pages only hint at it (model card slug, "Daily
+  Papers" page: Prism and RRAttention abstracts), so the definition is a
+  reading, see the design doc.
 * ``attention`` -- the plain masked-softmax definition
   ``O = softmax(Q K^T / sqrt(d) + mask) V`` with grouped KV heads, for prefill
   and for one-token decode that reuses the prefill route (technical summary,
@@ -32,6 +36,7 @@ torch Linear) and invariants; none is "parity unpinned".
 
 from .router import pool_positions, pool_mean, router_mlp, threshold_route, route_requests
 from .mask import num_blocks, block_mask, mask_to_csr, mask_row_count, mask_nnz
+from .dynmask import pool_blocks, coarse_logits, block_probs, select_blocks, dynamic_block_mask
 from .attention import (
     allowed_matrix,
     attention_probs,
@@ -44,6 +49,7 @@ from .attention import (
 __all__ = [
     "pool_positions", "pool_mean", "router_mlp", "threshold_route", "route_requests",
     "num_blocks", "block_mask", "mask_to_csr", "mask_row_count", "mask_nnz",
+    "pool_blocks", "coarse_logits", "block_probs", "select_blocks", "dynamic_block_mask",
     "allowed_matrix", "attention_probs", "attention_prefill",
     "attention_prefill_varlen", "attention_decode", "attention_prefill_soft",
 ]
