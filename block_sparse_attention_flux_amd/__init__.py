@@ -24,6 +24,7 @@ _LIB = _lib.load()
 
 __all__ = [
     "SAParams", "FluxError", "route", "route_workspace_size", "mask_blocks", "mask_nnz", "build_block_mask",
+    "build_block_mask_dynamic",
     "attn_prefill", "attn_prefill_soft", "decode_workspace_size", "decode_workspace", "attn_decode", "status_str",
     "kv_rows", "kv_cache", "kv_store_prefill", "kv_append", "attn_decode_sa_compact",
     "probe_mfma", "probe_read",
@@ -135,6 +136,31 @@ def build_block_mask(seqlen, sa, device="cuda", dense=True):
                                       _ptr(row_ptr), _ptr(col_idx), _stream(row_ptr.device))
     _check(code, "flux_build_block_mask")
     return mask, row_ptr, col_idx[:nnz]
+
+
+def build_block_mask_dynamic(q, k, block_size, sink_blocks, tau, max_blocks=0, softmax_scale=None):
+    """Content-aware SA block mask of one sequence (flux_build_block_mask_dynamic):
+    (row_ptr int32 [nb+1], col_idx int32 [nb (nb+1) / 2]); the first
+    row_ptr[nb] columns are the mask.  q [S][hq][d], k [S][hkv][d] bf16."""
+    S, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (S, hkv, d):
+        raise ValueError("k must be [S][hkv][head_dim] like q")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    nb = (S + int(block_size) - 1) // int(block_size)
+    cap = nb * (nb + 1) // 2
+    row_ptr = torch.empty(nb + 1, dtype=torch.int32, device=q.device)
+    col_idx = torch.empty(cap, dtype=torch.int32, device=q.device)
+    ws_bytes = int(_LIB.flux_dynamic_mask_workspace_size(S, hq, hkv, d, int(block_size)))
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    p = _lib.DynParamsC(int(block_size), int(sink_blocks), float(tau), int(max_blocks))
+    code = _LIB.flux_build_block_mask_dynamic(
+        _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), S, hq, hkv, d,
+        float(softmax_scale), p, _ptr(row_ptr), _ptr(col_idx), cap, _ptr(ws), ws.numel(),
+        _stream(q.device))
+    _check(code, "flux_build_block_mask_dynamic")
+    return row_ptr, col_idx
 
 
 def _route_fn(route, hkv, layer_fn, head_fn, what):

@@ -24,6 +24,11 @@ class SAParamsC(ctypes.Structure):
                 ("local_blocks", ctypes.c_int32)]
 
 
+class DynParamsC(ctypes.Structure):
+    _fields_ = [("block_size", ctypes.c_int32), ("sink_blocks", ctypes.c_int32),
+                ("tau", ctypes.c_float), ("max_blocks", ctypes.c_int32)]
+
+
 # (name, restype, argtypes) for every symbol of include/flux.h
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -36,6 +41,9 @@ SIGNATURES = [
     ("flux_mask_blocks", ctypes.c_int64, [_I, SAParamsC]),
     ("flux_mask_nnz", ctypes.c_int64, [_I, SAParamsC]),
     ("flux_build_block_mask", _I, [_I, SAParamsC, _P, _P, _P, _P]),
+    ("flux_dynamic_mask_workspace_size", _S, [_I, _I, _I, _I, _I]),
+    ("flux_build_block_mask_dynamic", _I, [_P, _P, _I, _I, _I, _I, _F, DynParamsC, _P, _P,
+                                           ctypes.c_int64, _P, _S, _P]),
     ("flux_attn_prefill", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P, _P,
                                _I, SAParamsC, _P]),
     ("flux_attn_decode_workspace_size", _S, [_I, _I, _I, _I, _I]),

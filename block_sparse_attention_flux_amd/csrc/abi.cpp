@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cstdint>
 
 #include "flux_internal.h"
 
@@ -186,6 +187,39 @@ flux_status flux_build_block_mask(int32_t seqlen, flux_sa_params p, uint8_t* mas
   return from_hip(flux::launch_build_mask(static_cast<int32_t>(nb), p.sink_blocks, p.local_blocks,
                                           mask_out, row_ptr, col_idx,
                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t flux_dynamic_mask_workspace_size(int32_t seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
+                                        int32_t block_size) {
+  if (seqlen < 1 || hq < 1 || hkv < 1 || head_dim < 1 || block_size < 1) return 0;
+  return flux::dynamic_mask_workspace_bytes(seqlen, hq, hkv, head_dim, block_size);
+}
+
+flux_status flux_build_block_mask_dynamic(const uint16_t* q, const uint16_t* k, int32_t seqlen,
+                                          int32_t hq, int32_t hkv, int32_t head_dim,
+                                          float softmax_scale, flux_dyn_params p, int32_t* row_ptr,
+                                          int32_t* col_idx, int64_t col_capacity, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k == nullptr || row_ptr == nullptr || col_idx == nullptr)
+    return FLUX_ERR_INVALID_ARG;
+  if (seqlen < 1 || hq < 1 || hkv < 1 || hq % hkv != 0) return FLUX_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.0f) || softmax_scale > 1e30f) return FLUX_ERR_INVALID_ARG;
+  if (!(p.tau >= 0.0f) || p.tau > 1e30f || p.sink_blocks < 0 || p.max_blocks < 0)
+    return FLUX_ERR_INVALID_ARG;
+  if (!head_dim_supported(head_dim) || !block_supported(p.block_size)) return FLUX_ERR_UNSUPPORTED;
+  if (hq / hkv > 16 || hq > flux::kMaxDynHeads) return FLUX_ERR_UNSUPPORTED;
+  const int64_t nb = (static_cast<int64_t>(seqlen) + p.block_size - 1) / p.block_size;
+  if (nb > flux::kMaxDynBlocks) return FLUX_ERR_UNSUPPORTED;
+  if (col_capacity < nb * (nb + 1) / 2) return FLUX_ERR_INVALID_ARG;
+  const size_t need = flux::dynamic_mask_workspace_bytes(seqlen, hq, hkv, head_dim, p.block_size);
+  if (workspace == nullptr || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return FLUX_ERR_WORKSPACE;
+  flux::DynMaskParams dp{};
+  dp.q = q; dp.k = k; dp.seqlen = seqlen; dp.hq = hq; dp.hkv = hkv; dp.head_dim = head_dim;
+  dp.block_size = p.block_size; dp.sink_blocks = p.sink_blocks; dp.max_blocks = p.max_blocks;
+  dp.scale = softmax_scale; dp.tau = p.tau;
+  dp.row_ptr = row_ptr; dp.col_idx = col_idx; dp.workspace = workspace;
+  return from_hip(flux::launch_dynamic_mask(dp, static_cast<hipStream_t>(stream)));
 }
 
 flux_status flux_attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -74,6 +74,23 @@ hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, const 
 hipError_t launch_build_mask(int32_t nb, int32_t sink, int32_t local, uint8_t* mask,
                              int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
 
+// Content-aware mask (dynmask.hip): limits of the one-workgroup-per-row
+// selection kernel (query heads staged in LDS, one probability per block).
+constexpr int32_t kMaxDynHeads = 64;
+constexpr int32_t kMaxDynBlocks = 4096;
+struct DynMaskParams {
+  const uint16_t* q;  // [seqlen][hq][d] bf16
+  const uint16_t* k;  // [seqlen][hkv][d] bf16
+  int32_t seqlen, hq, hkv, head_dim, block_size, sink_blocks, max_blocks;
+  float scale, tau;
+  int32_t* row_ptr;   // [nb + 1]
+  int32_t* col_idx;   // capacity nb (nb + 1) / 2
+  void* workspace;    // dynamic_mask_workspace_bytes
+};
+size_t dynamic_mask_workspace_bytes(int32_t seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
+                                    int32_t block_size);
+hipError_t launch_dynamic_mask(const DynMaskParams& p, hipStream_t s);
+
 // Workspace of the router: pooled vectors then hidden layers, fp32.
 size_t route_workspace_bytes(int32_t n_req, int32_t d_in, int32_t h1);
 hipError_t launch_route(const void* hidden, int32_t bf16, const int32_t* cu, int32_t n_req,

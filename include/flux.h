@@ -118,6 +118,52 @@ flux_status flux_build_block_mask(int32_t seqlen, flux_sa_params p, uint8_t* mas
                                   int32_t* row_ptr, int32_t* col_idx, void* stream);
 
 /*
+ * flux_build_block_mask_dynamic -- a content-aware SA block mask for one
+ * sequence.  The pages only hint at a content-based pattern (the model
+ * card's address slug); the "Daily Papers" page (hugingapi.com, search
+ * "Head-Centric Sparse Attention") describes block importance from
+ * coarse-grained attention between mean-pooled blocks (Prism abstract) and an
+ * adaptive Top-tau block selection (RRAttention abstract).  The definition
+ * built here:
+ *   qbar[i][h], kbar[j][g]  means of the rows of block i of q / block j of k
+ *                           (a shorter last block averages its own rows);
+ *   P[i][j]  mean over the query heads h of the softmax over j <= i of
+ *            softmax_scale * qbar[i][h] . kbar[j][h / (hq / hkv)];
+ *   row i keeps its sink blocks (j < sink_blocks) and its diagonal block,
+ *   then the other blocks j <= i by decreasing P (ties: smaller j first)
+ *   while the mass taken is below tau and the row holds fewer than
+ *   max_blocks blocks (max_blocks 0: no cap).
+ * The output is the CSR form that flux_attn_prefill and flux_attn_decode read
+ * as their SA mask (nb = ceil(seqlen / block_size) rows, columns increasing).
+ * The selection is decided in fp32: a block whose cumulative mass lands within
+ * rounding of tau may be kept by one implementation and not by another.
+ *
+ * q [device] bf16 [seqlen][hq][head_dim];  k [device] bf16 [seqlen][hkv][head_dim]
+ * row_ptr  [device] int32 [nb+1], written;
+ * col_idx  [device] int32 [col_capacity], col_capacity >= nb (nb + 1) / 2;
+ *          the first row_ptr[nb] entries are written
+ * workspace [device], 16-byte aligned, >= flux_dynamic_mask_workspace_size(...)
+ *          bytes; owned by the caller, overwritten.
+ * Supported: head_dim in {64, 128}, block_size in {64, 128}, hq % hkv == 0,
+ *   hq / hkv <= 16, hq <= 64, nb <= 4096.  tau >= 0 (tau >= 1 keeps every
+ *   causal block unless capped), sink_blocks >= 0, max_blocks >= 0, scale > 0.
+ */
+typedef struct {
+  int32_t block_size;   /* B: 64 or 128 */
+  int32_t sink_blocks;  /* always-kept leading blocks */
+  float tau;            /* probability mass a row must reach */
+  int32_t max_blocks;   /* cap on blocks per row; 0 = none */
+} flux_dyn_params;
+
+size_t flux_dynamic_mask_workspace_size(int32_t seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
+                                        int32_t block_size);
+flux_status flux_build_block_mask_dynamic(const uint16_t* q, const uint16_t* k, int32_t seqlen,
+                                          int32_t hq, int32_t hkv, int32_t head_dim,
+                                          float softmax_scale, flux_dyn_params p, int32_t* row_ptr,
+                                          int32_t* col_idx, int64_t col_capacity, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/*
  * flux_attn_prefill -- one attention layer over a packed batch of prompts.
  * FA: causal softmax attention; SA: the same restricted to the active blocks
  * of the mask (abstract: each layer runs FA or SA; model card: SA is

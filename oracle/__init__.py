@@ -36,7 +36,8 @@ torch Linear) and invariants; none is "parity unpinned".
 
 from .router import pool_positions, pool_mean, router_mlp, threshold_route, route_requests
 from .mask import num_blocks, block_mask, mask_to_csr, mask_row_count, mask_nnz
-from .dynmask import pool_blocks, coarse_logits, block_probs, select_blocks, dynamic_block_mask
+from .dynmask import (pool_blocks, coarse_logits, block_probs, block_probs_rows, select_row, select_blocks,
+                      dynamic_block_mask)
 from .attention import (
     allowed_matrix,
     attention_probs,
@@ -49,7 +50,8 @@ from .attention import (
 __all__ = [
     "pool_positions", "pool_mean", "router_mlp", "threshold_route", "route_requests",
     "num_blocks", "block_mask", "mask_to_csr", "mask_row_count", "mask_nnz",
-    "pool_blocks", "coarse_logits", "block_probs", "select_blocks", "dynamic_block_mask",
+    "pool_blocks", "coarse_logits", "block_probs", "block_probs_rows", "select_row", "select_blocks",
+    "dynamic_block_mask",
     "allowed_matrix", "attention_probs", "attention_prefill",
     "attention_prefill_varlen", "attention_decode", "attention_prefill_soft",
 ]

@@ -79,26 +79,51 @@ def block_probs(q, k, block_size, scale=None):
     return P / hq
 
 
+def block_probs_rows(q, k, block_size, rows, scale=None):
+    """Rows ``rows`` of ``P`` by the same definition with numpy matrix
+    products over the pooled blocks (for long sequences; pinned against
+    ``block_probs``).  Returns ``[len(rows), nb]``."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    hq, hkv, d = q.shape[1], k.shape[1], q.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    qb = pool_blocks(q, block_size)  # [nb, hq, d]
+    kb = pool_blocks(k, block_size)  # [nb, hkv, d]
+    nb = qb.shape[0]
+    group = hq // hkv
+    out = np.zeros((len(rows), nb))
+    for n, i in enumerate(rows):
+        for h in range(hq):
+            z = scale * (kb[:i + 1, h // group, :] @ qb[i, h])
+            e = np.exp(z - z.max())
+            out[n, :i + 1] += e / e.sum()
+    return out / hq
+
+
+def select_row(p, i, tau, sink_blocks, max_blocks=0):
+    """Blocks kept in row ``i`` given that row's probabilities ``p`` (length
+    > i), by the Top-tau rule (module docstring, step 3): a sorted list."""
+    mandatory = [j for j in range(i + 1) if j < sink_blocks or j == i]
+    keep = list(mandatory)
+    mass = sum(p[j] for j in mandatory)
+    others = [j for j in range(i + 1) if j not in mandatory]
+    others.sort(key=lambda j: (-p[j], j))
+    for j in others:
+        if mass >= tau or (max_blocks > 0 and len(keep) >= max_blocks):
+            break
+        keep.append(j)
+        mass += p[j]
+    return sorted(keep)
+
+
 def select_blocks(P, tau, sink_blocks, max_blocks=0):
-    """Dense uint8 mask ``[nb, nb]`` from the block probabilities by the Top-tau
-    rule (module docstring, step 3)."""
+    """Dense uint8 mask ``[nb, nb]``: ``select_row`` for every row of ``P``."""
     P = np.asarray(P, dtype=np.float64)
     nb = P.shape[0]
     m = np.zeros((nb, nb), dtype=np.uint8)
     for i in range(nb):
-        mandatory = [j for j in range(i + 1) if j < sink_blocks or j == i]
-        for j in mandatory:
-            m[i, j] = 1
-        mass = sum(P[i, j] for j in mandatory)
-        count = len(mandatory)
-        others = [j for j in range(i + 1) if j not in mandatory]
-        others.sort(key=lambda j: (-P[i, j], j))
-        for j in others:
-            if mass >= tau or (max_blocks > 0 and count >= max_blocks):
-                break
-            m[i, j] = 1
-            mass += P[i, j]
-            count += 1
+        m[i, select_row(P[i], i, tau, sink_blocks, max_blocks)] = 1
     return m
 
 

@@ -31,7 +31,7 @@ def declared_symbols(header=HEADER):
 
 def test_exports_every_declared_symbol():
     syms = declared_symbols()
-    assert len(syms) == 16, syms
+    assert len(syms) == 18, syms
     raw = ctypes.CDLL(LIB)
     for s in syms:
         assert hasattr(raw, s), s
@@ -233,3 +233,37 @@ def test_head_route_and_soft_validation():
     assert dec(route=NULL) == _lib.FLUX_ERR_INVALID_ARG
     assert dec(w=NULL) == _lib.FLUX_ERR_WORKSPACE
     assert dec(wsb=ws - 1) == _lib.FLUX_ERR_WORKSPACE
+
+
+def test_dynamic_mask_workspace_size_and_validation():
+    """flux_build_block_mask_dynamic: workspace formula (pooled Q and K in fp32,
+    one count per row, a row-stride column buffer) and host-side rejections."""
+    S, hq, hkv, d, B = 32768, 32, 8, 128, 128
+    nb = S // B
+    ws = lib.flux_dynamic_mask_workspace_size(S, hq, hkv, d, B)
+    assert ws == (nb * hq * d + nb * hkv * d) * 4 + nb * 4 + nb * nb * 4
+    assert lib.flux_dynamic_mask_workspace_size(0, hq, hkv, d, B) == 0
+    DP = _lib.DynParamsC
+    W = ctypes.c_void_p(0x2000)
+    cap = nb * (nb + 1) // 2
+
+    def call(q=FAKE, k=FAKE, s=S, h=hq, hk=hkv, dd=d, scale=0.088, p=None, rp=FAKE, ci=FAKE, c=cap, w=W, wb=ws):
+        p = p or DP(B, 1, 0.9, 17)
+        return lib.flux_build_block_mask_dynamic(q, k, s, h, hk, dd, scale, p, rp, ci, c, w, wb, NULL)
+    assert call(q=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(rp=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(h=30) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(s=0) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(scale=0.0) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(p=DP(B, -1, 0.9, 0)) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(p=DP(B, 1, -0.5, 0)) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(p=DP(B, 1, float("nan"), 0)) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(p=DP(B, 1, 0.9, -3)) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(dd=96) == _lib.FLUX_ERR_UNSUPPORTED
+    assert call(p=DP(32, 1, 0.9, 0)) == _lib.FLUX_ERR_UNSUPPORTED
+    assert call(h=128, hk=8) == _lib.FLUX_ERR_UNSUPPORTED       # group of 16 fits, 128 heads do not
+    assert call(s=4096 * 128 + 1) == _lib.FLUX_ERR_UNSUPPORTED  # 4097 blocks
+    assert call(c=cap - 1) == _lib.FLUX_ERR_INVALID_ARG
+    assert call(w=NULL) == _lib.FLUX_ERR_WORKSPACE
+    assert call(wb=ws - 1) == _lib.FLUX_ERR_WORKSPACE
+    assert call(w=ctypes.c_void_p(0x2008)) == _lib.FLUX_ERR_WORKSPACE  # not 16-byte aligned

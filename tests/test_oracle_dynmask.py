@@ -160,3 +160,12 @@ def test_greedy_prefix_and_minimality():
             assert base + P[i, chosen[:-1]].sum() < tau  # the last one was still needed
         full = base + P[i, chosen].sum()
         assert full >= tau or len(chosen) == len(cand)
+
+
+def test_block_probs_rows_matches_loops():
+    q, k = _qk(70, 4, 2, 8, 23)
+    P = oracle.block_probs(q, k, 8)
+    rows = [0, 3, 8]
+    np.testing.assert_allclose(oracle.block_probs_rows(q, k, 8, rows), P[rows], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(oracle.block_probs_rows(q, k, 8, rows, 0.21),
+                               oracle.block_probs(q, k, 8, 0.21)[rows], rtol=1e-12, atol=1e-15)
