@@ -17,12 +17,15 @@
 // Output: the same CSR form as the static builder (columns ascending), which
 // the prefill and decode kernels take as their SA mask.
 //
-// Three kernels: block means of Q and K (HBM-bound, one read of each);
-// one workgroup per mask row for the probabilities and the selection (the
-// candidate at sorted rank r is kept iff the mass of the r candidates ranked
-// before it, plus the mandatory blocks' mass, is below tau: ranks come from
-// pairwise comparisons, so no sort is needed); one workgroup per row for the
-// CSR offsets (a sum over the earlier rows' counts) and the copy.
+// Four kernels: block means of Q and K (HBM-bound, one read of each); one
+// workgroup per (mask row, KV head) for the logits and softmax of that head
+// group, summed over its query heads (written per group, then added in a
+// fixed order, so the result does not depend on scheduling); one workgroup
+// per mask row for the selection (the candidate at sorted rank r is kept iff
+// the mass of the r candidates ranked before it, plus the mandatory blocks'
+// mass, is below tau: ranks come from pairwise comparisons, so no sort is
+// needed); one workgroup per row for the CSR offsets (a sum over the earlier
+// rows' counts) and the copy.
 #include "flux_device.h"
 #include "flux_internal.h"
 
@@ -34,12 +37,14 @@ constexpr int kWaves = kThreads / 64;
 
 // (1) Mean of the rows of block i for one head of Q (y < hq) or K.  Thread t
 // sums 16-byte chunk t % CH of rows t / CH, t / CH + RL, ...; the partial sums
-// are added in LDS in a fixed order.
+// are added in LDS in a fixed order.  qbar is [nb][hq][D]; kbar is stored
+// transposed, [hkv][D][nb], so that consecutive key blocks are consecutive
+// words for the probability kernel.
 template <int D>
 __global__ __launch_bounds__(kThreads) void pool_kernel(const uint16_t* __restrict__ q,
                                                         const uint16_t* __restrict__ k, int32_t S,
-                                                        int32_t hq, int32_t hkv, int32_t B,
-                                                        float* __restrict__ qbar, float* __restrict__ kbar) {
+                                                        int32_t hq, int32_t hkv, int32_t B, int32_t nb,
+                                                        float* __restrict__ qbar, float* __restrict__ kbar_t) {
   constexpr int CH = D / 8;
   constexpr int RL = kThreads / CH;
   __shared__ float part[RL][D];
@@ -51,6 +56,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const uint16_t* __restri
   const int r0 = i * B, r1 = min(S, r0 + B);
   const int c = threadIdx.x % CH, rl = threadIdx.x / CH;
   float acc[8] = {};
+#pragma unroll 4
   for (int r = r0 + rl; r < r1; r += RL) {
     const u32x4 v = ld16(src + (static_cast<size_t>(r) * H + h) * D + c * 8);
 #pragma unroll
@@ -65,17 +71,22 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const uint16_t* __restri
   if (threadIdx.x < D) {
     float s = 0.0f;
     for (int t = 0; t < RL; ++t) s += part[t][threadIdx.x];
-    float* dst = is_q ? qbar : kbar;
-    dst[(static_cast<size_t>(i) * H + h) * D + threadIdx.x] = s / static_cast<float>(r1 - r0);
+    const float mean = s / static_cast<float>(r1 - r0);
+    if (is_q)
+      qbar[(static_cast<size_t>(i) * hq + h) * D + threadIdx.x] = mean;
+    else
+      kbar_t[(static_cast<size_t>(h) * D + threadIdx.x) * nb + i] = mean;
   }
 }
 
-// Workgroup reductions over kThreads values per slot (n slots at once):
-// lanes first (a fixed butterfly), then the waves in order.
+// Workgroup reduction of N values per thread (slots 0 .. n-1): lanes first
+// (a fixed butterfly), then the waves in order; every thread gets the result.
 template <int N>
 __device__ __forceinline__ void block_reduce(float (&v)[N], int n, bool is_max, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int s = 0; s < n; ++s) {
+#pragma unroll
+  for (int s = 0; s < N; ++s) {
+    if (s >= n) break;
     float x = v[s];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -85,80 +96,116 @@ __device__ __forceinline__ void block_reduce(float (&v)[N], int n, bool is_max, 
     v[s] = x;
   }
   __syncthreads();
-  if (lane == 0)
-    for (int s = 0; s < n; ++s) red[wave * N + s] = v[s];
+  if (lane == 0) {
+#pragma unroll
+    for (int s = 0; s < N; ++s)
+      if (s < n) red[wave * N + s] = v[s];
+  }
   __syncthreads();
-  for (int s = 0; s < n; ++s) {
+#pragma unroll
+  for (int s = 0; s < N; ++s) {
+    if (s >= n) break;
     float x = red[s];
     for (int w = 1; w < kWaves; ++w) x = is_max ? fmaxf(x, red[w * N + s]) : x + red[w * N + s];
     v[s] = x;
   }
 }
 
-// (2) One workgroup per query block i: P[i][0..i] and the selection.
-template <int D>
-__global__ __launch_bounds__(kThreads) void select_kernel(const float* __restrict__ qbar,
-                                                          const float* __restrict__ kbar, int32_t nb,
-                                                          int32_t hq, int32_t hkv, float scale,
-                                                          int32_t sink, float tau, int32_t max_blocks,
+// (2a) One workgroup per (query block i, KV head g): the logits of the query
+// heads of g against key blocks j <= i, their softmax over j, and the sum over
+// those heads of the probabilities, part[i][g][j].  Thread t owns key blocks
+// t, t + 256, ... (at most kOwn).  kGroup is the GQA group size rounded up to
+// a power of two (heads past the group are skipped).
+template <int D, int kGroup>
+__global__ __launch_bounds__(kThreads) void probs_kernel(const float* __restrict__ qbar,
+                                                         const float* __restrict__ kbar_t, int32_t nb,
+                                                         int32_t hq, int32_t hkv, float scale,
+                                                         float* __restrict__ part) {
+  constexpr int kOwn = kMaxDynBlocks / kThreads;  // key blocks per thread
+  __shared__ __attribute__((aligned(16))) float qs[kGroup * D];  // scale * qbar[i][h] of group g
+  __shared__ float red[kWaves * kGroup];
+
+  const int i = blockIdx.x, g = blockIdx.y, n = i + 1, tid = threadIdx.x;
+  const int group = hq / hkv;
+  for (int e = tid; e < group * D; e += kThreads)
+    qs[e] = scale * qbar[(static_cast<size_t>(i) * hq + g * group) * D + e];
+  __syncthreads();
+
+  float z[kOwn][kGroup];
+#pragma unroll
+  for (int o = 0; o < kOwn; ++o) {
+    const int j = tid + o * kThreads;
+#pragma unroll
+    for (int hh = 0; hh < kGroup; ++hh) z[o][hh] = kNegInf;
+    if (j < n) {
+#pragma unroll
+      for (int hh = 0; hh < kGroup; ++hh) z[o][hh] = 0.0f;
+      const float* kb = kbar_t + static_cast<size_t>(g) * D * nb + j;
+#pragma unroll 2
+      for (int c = 0; c < D; c += 4) {
+        float kv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kv[e] = kb[static_cast<size_t>(c + e) * nb];
+#pragma unroll
+        for (int hh = 0; hh < kGroup; ++hh)
+          if (hh < group) {
+            const f32x4 qv = *reinterpret_cast<const f32x4*>(qs + hh * D + c);
+            z[o][hh] += qv[0] * kv[0] + qv[1] * kv[1] + qv[2] * kv[2] + qv[3] * kv[3];
+          }
+      }
+    }
+  }
+  float mx[kGroup], sm[kGroup];
+#pragma unroll
+  for (int hh = 0; hh < kGroup; ++hh) {
+    mx[hh] = kNegInf;
+#pragma unroll
+    for (int o = 0; o < kOwn; ++o) mx[hh] = fmaxf(mx[hh], z[o][hh]);
+  }
+  block_reduce<kGroup>(mx, group, true, red);
+#pragma unroll
+  for (int hh = 0; hh < kGroup; ++hh) {
+    sm[hh] = 0.0f;
+    if (hh < group) {
+#pragma unroll
+      for (int o = 0; o < kOwn; ++o) {
+        z[o][hh] = fast_exp2((z[o][hh] - mx[hh]) * kLog2e);  // 0 for blocks past the row
+        sm[hh] += z[o][hh];
+      }
+    }
+  }
+  block_reduce<kGroup>(sm, group, false, red);
+#pragma unroll
+  for (int hh = 0; hh < kGroup; ++hh) sm[hh] = 1.0f / sm[hh];
+#pragma unroll
+  for (int o = 0; o < kOwn; ++o) {
+    const int j = tid + o * kThreads;
+    if (j < n) {
+      float p = 0.0f;
+#pragma unroll
+      for (int hh = 0; hh < kGroup; ++hh)
+        if (hh < group) p += z[o][hh] * sm[hh];
+      part[(static_cast<size_t>(i) * hkv + g) * nb + j] = p;
+    }
+  }
+}
+
+// (2b) One workgroup per query block i: P[i][j] = (sum over g of part[i][g][j])
+// / hq, then the selection.
+__global__ __launch_bounds__(kThreads) void select_kernel(const float* __restrict__ part, int32_t nb,
+                                                          int32_t hq, int32_t hkv, int32_t sink,
+                                                          float tau, int32_t max_blocks,
                                                           int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ cols_tmp) {
-  constexpr int kMaxH = kMaxDynHeads;
-  __shared__ __attribute__((aligned(16))) float qs[kMaxH * D];  // scale * qbar[i][h]
   __shared__ float P[kMaxDynBlocks];
-  __shared__ float red[kWaves * kMaxH];
-  __shared__ float stat_m[kMaxH], stat_l[kMaxH];
+  __shared__ float red[kWaves];
   __shared__ int32_t scan[kWaves];
 
   const int i = blockIdx.x, n = i + 1, tid = threadIdx.x;
-  const int group = hq / hkv;
-  for (int e = tid; e < hq * D; e += kThreads) qs[e] = scale * qbar[static_cast<size_t>(i) * hq * D + e];
-  __syncthreads();
-
-  // logits of key block j for the query heads of KV head g, into z[0..group)
-  auto logits = [&](int j, int g, float (&z)[16]) {
-    const f32x4* kb = reinterpret_cast<const f32x4*>(kbar + (static_cast<size_t>(j) * hkv + g) * D);
-    for (int hh = 0; hh < group; ++hh) z[hh] = 0.0f;
-    for (int c4 = 0; c4 < D / 4; ++c4) {
-      const f32x4 kv = kb[c4];
-      for (int hh = 0; hh < group; ++hh) {
-        const f32x4 qv = *reinterpret_cast<const f32x4*>(qs + (g * group + hh) * D + c4 * 4);
-        z[hh] += qv[0] * kv[0] + qv[1] * kv[1] + qv[2] * kv[2] + qv[3] * kv[3];
-      }
-    }
-  };
-
-  // pass 1: per-head max over the causal key blocks; pass 2: per-head sum
-  for (int pass = 0; pass < 2; ++pass) {
-    float acc[kMaxH];
-    for (int h = 0; h < hq; ++h) acc[h] = pass == 0 ? kNegInf : 0.0f;
-    for (int j = tid; j < n; j += kThreads)
-      for (int g = 0; g < hkv; ++g) {
-        float z[16];
-        logits(j, g, z);
-        for (int hh = 0; hh < group; ++hh) {
-          const int h = g * group + hh;
-          acc[h] = pass == 0 ? fmaxf(acc[h], z[hh]) : acc[h] + fast_exp2((z[hh] - stat_m[h]) * kLog2e);
-        }
-      }
-    block_reduce<kMaxH>(acc, hq, pass == 0, red);
-    __syncthreads();
-    if (tid == 0)
-      for (int h = 0; h < hq; ++h) (pass == 0 ? stat_m : stat_l)[h] = acc[h];
-    __syncthreads();
-  }
-  // pass 3: P[j] = mean over heads of the softmax
   const float inv_h = 1.0f / static_cast<float>(hq);
   for (int j = tid; j < n; j += kThreads) {
     float p = 0.0f;
-    for (int g = 0; g < hkv; ++g) {
-      float z[16];
-      logits(j, g, z);
-      for (int hh = 0; hh < group; ++hh) {
-        const int h = g * group + hh;
-        p += fast_exp2((z[hh] - stat_m[h]) * kLog2e) / stat_l[h];
-      }
-    }
+    for (int g = 0; g < hkv; ++g) p += part[(static_cast<size_t>(i) * hkv + g) * nb + j];
     P[j] = p * inv_h;
   }
   __syncthreads();
@@ -184,13 +231,12 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float* __restric
         const float pj = P[j];
         int rank = 0;
         float before = 0.0f;
+#pragma unroll 8
         for (int kk = 0; kk < n; ++kk) {
-          if (mandatory(kk)) continue;
           const float pk = P[kk];
-          if (pk > pj || (pk == pj && kk < j)) {
-            ++rank;
-            before += pk;
-          }
+          const bool ahead = !mandatory(kk) && (pk > pj || (pk == pj && kk < j));
+          rank += ahead ? 1 : 0;
+          before += ahead ? pk : 0.0f;
         }
         on = base + before < tau && (max_blocks == 0 || n_mand + rank < max_blocks);
       }
@@ -231,31 +277,50 @@ __global__ __launch_bounds__(kThreads) void csr_kernel(const int32_t* __restrict
   }
 }
 
+template <int D>
+void launch_probs(int group, dim3 grid, hipStream_t s, const float* qbar, const float* kbar_t, int nb, int hq,
+                  int hkv, float scale, float* part) {
+  if (group <= 1)
+    probs_kernel<D, 1><<<grid, kThreads, 0, s>>>(qbar, kbar_t, nb, hq, hkv, scale, part);
+  else if (group <= 2)
+    probs_kernel<D, 2><<<grid, kThreads, 0, s>>>(qbar, kbar_t, nb, hq, hkv, scale, part);
+  else if (group <= 4)
+    probs_kernel<D, 4><<<grid, kThreads, 0, s>>>(qbar, kbar_t, nb, hq, hkv, scale, part);
+  else if (group <= 8)
+    probs_kernel<D, 8><<<grid, kThreads, 0, s>>>(qbar, kbar_t, nb, hq, hkv, scale, part);
+  else
+    probs_kernel<D, 16><<<grid, kThreads, 0, s>>>(qbar, kbar_t, nb, hq, hkv, scale, part);
+}
+
 }  // namespace
 
 size_t dynamic_mask_workspace_bytes(int32_t seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
                                     int32_t block_size) {
   const size_t nb = (static_cast<size_t>(seqlen) + block_size - 1) / block_size;
-  return (nb * hq * head_dim + nb * hkv * head_dim) * sizeof(float) + nb * sizeof(int32_t) +
-         nb * nb * sizeof(int32_t);
+  return (nb * hq * head_dim + nb * hkv * head_dim + nb * hkv * nb) * sizeof(float) +
+         nb * sizeof(int32_t) + nb * nb * sizeof(int32_t);
 }
 
 hipError_t launch_dynamic_mask(const DynMaskParams& p, hipStream_t s) {
   const int nb = (p.seqlen + p.block_size - 1) / p.block_size;
   float* qbar = static_cast<float*>(p.workspace);
-  float* kbar = qbar + static_cast<size_t>(nb) * p.hq * p.head_dim;
-  int32_t* counts = reinterpret_cast<int32_t*>(kbar + static_cast<size_t>(nb) * p.hkv * p.head_dim);
+  float* kbar_t = qbar + static_cast<size_t>(nb) * p.hq * p.head_dim;
+  float* part = kbar_t + static_cast<size_t>(nb) * p.hkv * p.head_dim;
+  int32_t* counts = reinterpret_cast<int32_t*>(part + static_cast<size_t>(nb) * p.hkv * nb);
   int32_t* cols_tmp = counts + nb;
-  const dim3 pool_grid(nb, p.hq + p.hkv);
+  const dim3 pool_grid(nb, p.hq + p.hkv), probs_grid(nb, p.hkv);
+  const int group = p.hq / p.hkv;
   if (p.head_dim == 128) {
-    pool_kernel<128><<<pool_grid, kThreads, 0, s>>>(p.q, p.k, p.seqlen, p.hq, p.hkv, p.block_size, qbar, kbar);
-    select_kernel<128><<<nb, kThreads, 0, s>>>(qbar, kbar, nb, p.hq, p.hkv, p.scale, p.sink_blocks, p.tau,
-                                               p.max_blocks, counts, cols_tmp);
+    pool_kernel<128><<<pool_grid, kThreads, 0, s>>>(p.q, p.k, p.seqlen, p.hq, p.hkv, p.block_size, nb, qbar,
+                                                    kbar_t);
+    launch_probs<128>(group, probs_grid, s, qbar, kbar_t, nb, p.hq, p.hkv, p.scale, part);
   } else {
-    pool_kernel<64><<<pool_grid, kThreads, 0, s>>>(p.q, p.k, p.seqlen, p.hq, p.hkv, p.block_size, qbar, kbar);
-    select_kernel<64><<<nb, kThreads, 0, s>>>(qbar, kbar, nb, p.hq, p.hkv, p.scale, p.sink_blocks, p.tau,
-                                              p.max_blocks, counts, cols_tmp);
+    pool_kernel<64><<<pool_grid, kThreads, 0, s>>>(p.q, p.k, p.seqlen, p.hq, p.hkv, p.block_size, nb, qbar,
+                                                   kbar_t);
+    launch_probs<64>(group, probs_grid, s, qbar, kbar_t, nb, p.hq, p.hkv, p.scale, part);
   }
+  select_kernel<<<nb, kThreads, 0, s>>>(part, nb, p.hq, p.hkv, p.sink_blocks, p.tau, p.max_blocks, counts,
+                                        cols_tmp);
   csr_kernel<<<nb, kThreads, 0, s>>>(counts, cols_tmp, nb, p.row_ptr, p.col_idx);
   return hipGetLastError();
 }

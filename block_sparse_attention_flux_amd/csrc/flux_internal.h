@@ -77,7 +77,7 @@ hipError_t launch_build_mask(int32_t nb, int32_t sink, int32_t local, uint8_t* m
 // Content-aware mask (dynmask.hip): limits of the one-workgroup-per-row
 // selection kernel (query heads staged in LDS, one probability per block).
 constexpr int32_t kMaxDynHeads = 64;
-constexpr int32_t kMaxDynBlocks = 4096;
+constexpr int32_t kMaxDynBlocks = 1024;
 struct DynMaskParams {
   const uint16_t* q;  // [seqlen][hq][d] bf16
   const uint16_t* k;  // [seqlen][hkv][d] bf16

@@ -237,11 +237,12 @@ def test_head_route_and_soft_validation():
 
 def test_dynamic_mask_workspace_size_and_validation():
     """flux_build_block_mask_dynamic: workspace formula (pooled Q and K in fp32,
-    one count per row, a row-stride column buffer) and host-side rejections."""
+    per-KV-head probability sums, one count per row, a row-stride column
+    buffer) and host-side rejections."""
     S, hq, hkv, d, B = 32768, 32, 8, 128, 128
     nb = S // B
     ws = lib.flux_dynamic_mask_workspace_size(S, hq, hkv, d, B)
-    assert ws == (nb * hq * d + nb * hkv * d) * 4 + nb * 4 + nb * nb * 4
+    assert ws == (nb * hq * d + nb * hkv * d + nb * hkv * nb) * 4 + nb * 4 + nb * nb * 4
     assert lib.flux_dynamic_mask_workspace_size(0, hq, hkv, d, B) == 0
     DP = _lib.DynParamsC
     W = ctypes.c_void_p(0x2000)
@@ -262,7 +263,7 @@ def test_dynamic_mask_workspace_size_and_validation():
     assert call(dd=96) == _lib.FLUX_ERR_UNSUPPORTED
     assert call(p=DP(32, 1, 0.9, 0)) == _lib.FLUX_ERR_UNSUPPORTED
     assert call(h=128, hk=8) == _lib.FLUX_ERR_UNSUPPORTED       # group of 16 fits, 128 heads do not
-    assert call(s=4096 * 128 + 1) == _lib.FLUX_ERR_UNSUPPORTED  # 4097 blocks
+    assert call(s=1024 * 128 + 1) == _lib.FLUX_ERR_UNSUPPORTED  # 1025 blocks
     assert call(c=cap - 1) == _lib.FLUX_ERR_INVALID_ARG
     assert call(w=NULL) == _lib.FLUX_ERR_WORKSPACE
     assert call(wb=ws - 1) == _lib.FLUX_ERR_WORKSPACE
