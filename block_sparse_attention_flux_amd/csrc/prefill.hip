@@ -11,29 +11,34 @@
 //   row, so inactive K/V tiles are never loaded.  A wave skips the tiles
 //   that start past its last row (it still joins the block's barriers).
 //
-// Per key tile and wave (bf16 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulate):
-//   S^T[key][q] = K Q^T      A = K rows from LDS, B = Q kept in registers
-//   online softmax in the log2 domain; row max and row sum combine the two
-//   lane halves with v_permlane32_swap
-//   O^T[d][q] += V^T P^T     A = V^T via the LDS transpose read, B = P
-//   The transposed products put one query row in each lane (q = lane % 32),
-//   so softmax statistics and the O rescale are per-lane scalars and P lands
-//   directly in the B-operand layout of the second MFMA.  The row sum is
-//   taken over the same bf16 P that the second product uses (v_dot2c).
+// Per key tile and wave (bf16 MFMA v_mfma_f32_16x16x32_bf16, fp32 accumulate):
+//   S^T[key][q] = K Q^T      2 key halves x 2 row tiles of 16 x 16: four
+//                            independent accumulators; A = K from LDS, B = Q
+//                            kept in registers for the whole kernel
+//   online softmax in the log2 domain; a row lives on 4 lanes (l%16 + 16g),
+//   whose max and sum combine with v_permlane32_swap + v_permlane16_swap
+//   O^T[d][q] += V^T P^T     d/16 x 2 tiles, one 32-key k-step each; A = V^T
+//                            via the LDS transpose read, B = P
+//   The transposed products leave P in the B-operand layout of the second
+//   MFMA: its k index runs over the tile's keys in the order the S^T
+//   accumulator holds them in a lane, and V^T is read in the same order.
+//   The row sum is taken over the same bf16 P that the second product uses
+//   (v_dot2c).
 //
 // Data movement
 //   K and V tiles go global -> LDS directly (buffer_load_dwordx4 ... lds, no
 //   register staging) through a buffer resource whose range ends at the last
 //   key of the sequence, so a ragged last tile reads zeros.  K is row-major
-//   with XOR-swizzled 16-byte chunks, V in 128-byte blocks of 4 keys x 16 d;
-//   every LDS read below is bank-conflict free.  V^T operands come from
-//   ds_read_b64_tr_b16: within each 16-lane group, destination lane 4i+j
-//   receives element j of source lanes i, i+4, i+8, i+12, so four source
-//   lanes pointing at four keys deliver those keys' values of one d column.
-//   Two K and two V buffers live in four separate LDS arrays: tile n is
-//   computed from one pair while tile n+1 loads into the other.  With
-//   separate arrays the compiler can tell that the LDS reads never alias the
-//   DMA in flight and does not make them wait for it.
+//   with two 16-byte pad slots per row, V in 128-byte blocks of 4 keys x 16 d
+//   with the d block XORed by the key quad's parity; every LDS read below is
+//   bank-conflict free and addressed as a base register plus constant
+//   offsets.  V^T operands come from ds_read_b64_tr_b16: within each 16-lane
+//   group, destination lane 4i+j receives element j of source lanes i, i+4,
+//   i+8, i+12, so four source lanes pointing at four keys deliver those keys'
+//   values of one d column.  Two K and two V buffers live in four separate LDS
+//   arrays: tile n is computed from one pair while tile n+1 loads into the
+//   other.  With separate arrays the compiler can tell that the LDS reads
+//   never alias the DMA in flight and does not make them wait for it.
 //
 // The running max is only moved when a row's max grows by more than 2^8 (the
 // final normalisation divides by a sum taken with the same stale max, so the
