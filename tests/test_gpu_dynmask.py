@@ -177,3 +177,26 @@ def test_dynamic_mask_32k_sampled():
     counts = m.sum(axis=1)
     # random data: the rows are nearly uniform, so past row 18 the cap binds before tau
     assert counts.max() <= cap and counts[19:].min() == cap
+
+
+def test_decode_on_dynamic_mask():
+    """SA decode reads any CSR row, scattered blocks included: the dynamic mask
+    of a 3000-token prompt drives decode at several cached lengths (the mask
+    row is that of each sequence's last block), against the oracle's decode on
+    the same mask."""
+    from tests.test_gpu_parity import make_decode
+    S, hq, hkv, d, B = 3000, 8, 2, 128, 128
+    say("decode on a dynamic mask")
+    q, k = qk(S, hq, hkv, d, 61, planted=True)
+    row_ptr, col_idx = flux.build_block_mask_dynamic(q, k, B, 1, 0.5, 6)
+    nb = (S + B - 1) // B
+    m = csr_to_dense(row_ptr, col_idx, nb)
+    assert not np.array_equal(m, oracle.block_mask(nb, 1, 5))  # not a sink + window pattern
+    seqlens = [3000, 1777, 129, 1]
+    qd, kc, vc, sl = make_decode(len(seqlens), S, seqlens, hq, hkv, d, 62)
+    sa = flux.SAParams(B, 1, 5)
+    route = torch.tensor([[0]] * len(seqlens), dtype=torch.uint8, device=DEV)
+    out = flux.attn_decode(qd, kc, vc, sl, route, 0, row_ptr, col_idx, sa)
+    torch.cuda.synchronize()
+    ref = oracle.attention_decode(f32(qd), f32(kc), f32(vc), seqlens, False, m, B)
+    assert_attn_close(f32(out), ref, "decode on dynamic mask")
