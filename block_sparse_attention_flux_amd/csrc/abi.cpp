@@ -207,7 +207,7 @@ flux_status flux_build_block_mask_dynamic(const uint16_t* q, const uint16_t* k, 
   if (!(p.tau >= 0.0f) || p.tau > 1e30f || p.sink_blocks < 0 || p.max_blocks < 0)
     return FLUX_ERR_INVALID_ARG;
   if (!head_dim_supported(head_dim) || !block_supported(p.block_size)) return FLUX_ERR_UNSUPPORTED;
-  if (hq / hkv > 16 || hq > flux::kMaxDynHeads) return FLUX_ERR_UNSUPPORTED;
+  if (hq / hkv > 16) return FLUX_ERR_UNSUPPORTED;
   const int64_t nb = (static_cast<int64_t>(seqlen) + p.block_size - 1) / p.block_size;
   if (nb > flux::kMaxDynBlocks) return FLUX_ERR_UNSUPPORTED;
   if (col_capacity < nb * (nb + 1) / 2) return FLUX_ERR_INVALID_ARG;

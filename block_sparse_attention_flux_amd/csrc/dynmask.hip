@@ -86,14 +86,15 @@ __device__ __forceinline__ void block_reduce(float (&v)[N], int n, bool is_max, 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int s = 0; s < N; ++s) {
-    if (s >= n) break;
-    float x = v[s];
+    if (s < n) {
+      float x = v[s];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float y = __shfl_xor(x, o);
-      x = is_max ? fmaxf(x, y) : x + y;
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float y = __shfl_xor(x, o);
+        x = is_max ? fmaxf(x, y) : x + y;
+      }
+      v[s] = x;
     }
-    v[s] = x;
   }
   __syncthreads();
   if (lane == 0) {
@@ -104,10 +105,11 @@ __device__ __forceinline__ void block_reduce(float (&v)[N], int n, bool is_max, 
   __syncthreads();
 #pragma unroll
   for (int s = 0; s < N; ++s) {
-    if (s >= n) break;
-    float x = red[s];
-    for (int w = 1; w < kWaves; ++w) x = is_max ? fmaxf(x, red[w * N + s]) : x + red[w * N + s];
-    v[s] = x;
+    if (s < n) {
+      float x = red[s];
+      for (int w = 1; w < kWaves; ++w) x = is_max ? fmaxf(x, red[w * N + s]) : x + red[w * N + s];
+      v[s] = x;
+    }
   }
 }
 

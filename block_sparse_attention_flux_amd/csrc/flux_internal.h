@@ -74,9 +74,9 @@ hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, const 
 hipError_t launch_build_mask(int32_t nb, int32_t sink, int32_t local, uint8_t* mask,
                              int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
 
-// Content-aware mask (dynmask.hip): limits of the one-workgroup-per-row
-// selection kernel (query heads staged in LDS, one probability per block).
-constexpr int32_t kMaxDynHeads = 64;
+// Content-aware mask (dynmask.hip): most key blocks per row (each thread of
+// a 256-thread workgroup keeps up to 4 in registers, one probability per
+// block in LDS).
 constexpr int32_t kMaxDynBlocks = 1024;
 struct DynMaskParams {
   const uint16_t* q;  // [seqlen][hq][d] bf16

@@ -597,7 +597,9 @@ hipError_t launch_typed(const PrefillParams& p, hipStream_t s) {
   if (p.rsoft != nullptr) {  // two O accumulators: built for 2 waves per SIMD
     prefill_kernel<D, BM, kBN, 2, true><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
   } else {
-    prefill_kernel<D, BM, kBN, kOcc><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
+    // 64-row blocks: 2-wave workgroups whose tiles hold LDS for 2 waves per SIMD
+    constexpr int occ = BM == 128 ? kOcc : 2;
+    prefill_kernel<D, BM, kBN, occ><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
   }
   return hipGetLastError();
 }

@@ -145,7 +145,7 @@ flux_status flux_build_block_mask(int32_t seqlen, flux_sa_params p, uint8_t* mas
  * workspace [device], 16-byte aligned, >= flux_dynamic_mask_workspace_size(...)
  *          bytes; owned by the caller, overwritten.
  * Supported: head_dim in {64, 128}, block_size in {64, 128}, hq % hkv == 0,
- *   hq / hkv <= 16, hq <= 64, nb <= 1024.  tau >= 0 (tau >= 1 keeps every
+ *   hq / hkv <= 16, nb <= 1024.  tau >= 0 (tau >= 1 keeps every
  *   causal block unless capped), sink_blocks >= 0, max_blocks >= 0, scale > 0.
  */
 typedef struct {

@@ -262,7 +262,7 @@ def test_dynamic_mask_workspace_size_and_validation():
     assert call(p=DP(B, 1, 0.9, -3)) == _lib.FLUX_ERR_INVALID_ARG
     assert call(dd=96) == _lib.FLUX_ERR_UNSUPPORTED
     assert call(p=DP(32, 1, 0.9, 0)) == _lib.FLUX_ERR_UNSUPPORTED
-    assert call(h=128, hk=8) == _lib.FLUX_ERR_UNSUPPORTED       # group of 16 fits, 128 heads do not
+    assert call(h=64, hk=2) == _lib.FLUX_ERR_UNSUPPORTED        # GQA group of 32
     assert call(s=1024 * 128 + 1) == _lib.FLUX_ERR_UNSUPPORTED  # 1025 blocks
     assert call(c=cap - 1) == _lib.FLUX_ERR_INVALID_ARG
     assert call(w=NULL) == _lib.FLUX_ERR_WORKSPACE
