@@ -39,6 +39,12 @@
 //   arrays: tile n is computed from one pair while tile n+1 loads into the
 //   other.  With separate arrays the compiler can tell that the LDS reads
 //   never alias the DMA in flight and does not make them wait for it.
+//   A workgroup's scalars (sequence bounds, its mask row's CSR bounds, the
+//   route byte) arrive in one gathered load; an SA row's first 64 columns
+//   are held one per lane and picked with readlane, once per mask block.
+//   O leaves through LDS (each wave stages its 32 rows in one of the tile
+//   arrays after the last tile) so that the global stores are 16 bytes per
+//   lane and cover whole rows.
 //
 // The running max is only moved when a row's max grows by more than 2^8 (the
 // final normalisation divides by a sum taken with the same stale max, so the
@@ -66,8 +72,8 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) int32_t lds_i32;
 
 // LDS layouts (64 banks of 4 bytes; an 8-byte read is served 32 lanes per
 // pass):
@@ -373,9 +379,17 @@ struct WaveAttn {
                                                                  oacc[A][c][dt], 0, 0, 0);
   }
 
-  // O = w0 O_0 / l_0 (+ w1 O_1 / l_1); lane l writes d 16dt + 4(l/16) .. +3 of its two rows
-  __device__ __forceinline__ void store(uint16_t* out, int tok0, int hq, int head, int S,
-                                        float w0 = 1.0f, float w1 = 0.0f) const {
+  // O = w0 O_0 / l_0 (+ w1 O_1 / l_1), staged through this wave's LDS slice
+  // (32 rows of D bf16, free once the tile loop has ended) so that every
+  // global store writes 16 bytes per lane and whole rows per instruction.
+  // The slice is written in the accumulator layout (lane l: d 16dt + 4(l/16)
+  // .. +3 of its two rows) and read row-major; the 16-byte chunks of a row
+  // are XOR-swizzled by the row (D 128: row & 15; D 64: (row >> 1) & 7) so
+  // both passes are free of bank conflicts.
+  __device__ __forceinline__ void store(uint16_t* out, int tok0, int hq, int head, int S, lds_u8* stage,
+                                        int lane, float w0 = 1.0f, float w1 = 0.0f) const {
+    constexpr int CH = D / 8;  // 16-byte chunks per row
+    auto swz = [](int r) { return CH == 16 ? (r & 15) : ((r >> 1) & 7); };
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       float inv[NACC];
@@ -384,61 +398,68 @@ struct WaveAttn {
         const float lt = sum_quarters(sum_halves(l_run[a][c]));
         inv[a] = (lt > 0.0f ? 1.0f / lt : 0.0f) * (a == 0 ? w0 : w1);
       }
-      const int row = wrow0 + 16 * c + l16;
-      if (row < S) {
-        uint16_t* op = out + (static_cast<size_t>(tok0 + row) * hq + head) * D + 4 * grp;
+      const int r = 16 * c + l16;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          float o[4];
+      for (int dt = 0; dt < DT; ++dt) {
+        float o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[e] = oacc[0][c][dt][e] * inv[0];
-            if (NACC > 1) o[e] = __builtin_fmaf(oacc[NACC - 1][c][dt][e], inv[NACC - 1], o[e]);
-          }
-          *reinterpret_cast<u32x2*>(op + 16 * dt) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        for (int e = 0; e < 4; ++e) {
+          o[e] = oacc[0][c][dt][e] * inv[0];
+          if (NACC > 1) o[e] = __builtin_fmaf(oacc[NACC - 1][c][dt][e], inv[NACC - 1], o[e]);
         }
+        const int chunk = 2 * dt + (grp >> 1);
+        *reinterpret_cast<lds_u32x2*>(stage + r * (D * 2) + ((chunk ^ swz(r)) * 16) + (grp & 1) * 8) =
+            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
       }
+    }
+    constexpr int RPI = 64 / CH;  // rows per 16-byte-per-lane instruction
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = RPI * i + lane / CH, chunk = lane % CH;
+      const u32x4 v = *reinterpret_cast<const lds_u32x4*>(stage + r * (D * 2) + ((chunk ^ swz(r)) * 16));
+      if (wrow0 + r < S) st16(out + (static_cast<size_t>(tok0 + wrow0 + r) * hq + head) * D + chunk * 8, v);
     }
   }
 };
 
 // Query block's key tiles: FA = every tile up to the diagonal, SA = the
-// tiles of the blocks in the CSR row (columns clamped into [0, t]).  The first
-// kLdsCols columns of the row are staged in LDS once, so finding the next
-// tile's start never waits on a global load.
+// tiles of the blocks in the CSR row (columns clamped into [0, t]).  Each
+// wave keeps the row's first 64 columns one per lane (read with one load,
+// picked with readlane), so finding a tile's start needs no LDS and no
+// barrier; later columns, rare, are read from memory.
 template <int BM, int BN>
 struct TileList {
   static constexpr int TPB = BM / BN;  // key tiles per mask block
-  static constexpr int kLdsCols = 64;  // CSR entries staged in LDS
   const int32_t* col_idx;
-  const lds_i32* cols;
-  int rp0, n_tiles, t;
+  int rp0, n_tiles, t, col_lane;
   bool fa;
-  // Every thread of the workgroup calls this (it contains a barrier on the SA path).
-  __device__ __forceinline__ void init(const PrefillParams& p, int qt, int q_end, bool is_fa,
-                                       lds_i32* lds_cols, int tid, int nthreads) {
+  // rb, re: the mask row's CSR bounds (read by the caller beside the route)
+  __device__ __forceinline__ void init(const PrefillParams& p, int qt, bool is_fa, int rb, int re, int lane) {
     fa = is_fa;
     t = qt;
     col_idx = p.col_idx;
-    cols = lds_cols;
-    rp0 = 0;
+    rp0 = rb;
+    col_lane = 0;
+    n_tiles = 0;
+    if (!fa) {
+      const int n_blocks = max(re - rb, 0);
+      col_lane = lane < n_blocks ? col_idx[rp0 + lane] : 0;  // clamped when read
+      n_tiles = n_blocks * TPB;
+    }
+  }
+  // tiles of the query block ending at q_end (FA: up to the diagonal; SA:
+  // the CSR row without tiles that start past the block's last row)
+  __device__ __forceinline__ void trim(int q_end) {
     if (fa) {
       n_tiles = (q_end + BN - 1) / BN;
-    } else {
-      const int mrow = min(qt, p.mask_blocks - 1);
-      rp0 = p.row_ptr[mrow];
-      const int n_blocks = max(p.row_ptr[mrow + 1] - rp0, 0);
-      for (int i = tid; i < min(n_blocks, kLdsCols); i += nthreads)
-        lds_cols[i] = min(max(col_idx[rp0 + i], 0), t);
-      __syncthreads();
-      n_tiles = n_blocks * TPB;
-      while (n_tiles > 0 && start(n_tiles - 1) >= q_end) --n_tiles;
+      return;
     }
+    while (n_tiles > 0 && start(n_tiles - 1) >= q_end) --n_tiles;
   }
   __device__ __forceinline__ int start(int n) const {
     if (fa) return n * BN;
     const int bi = n / TPB;
-    const int blk = bi < kLdsCols ? cols[bi] : min(max(col_idx[rp0 + bi], 0), t);
+    const int blk = min(max(bi < 64 ? __builtin_amdgcn_readlane(col_lane, bi) : col_idx[rp0 + bi], 0), t);
     return blk * BM + (n % TPB) * BN;
   }
   // tiles a wave whose first row is wrow0 must see (up to its last row)
@@ -510,27 +531,43 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   decode_work(group, p.n_req, n_qt, p.hkv, p.route_heads > 1, hi, req, t, g);
   const int head = g * group + hi;
 
-  const int tok0 = p.cu_seqlens[req];
-  const int S = p.cu_seqlens[req + 1] - tok0;
+  // Sequence bounds, the mask row's CSR bounds and the route byte: one
+  // gathered load (lane i reads word i), so the workgroup pays a single
+  // memory round trip for all of them.  The route byte comes with the
+  // aligned word that holds it (that word never crosses a page).
+  const int mrow = min(t, p.mask_blocks - 1);
+  const uint8_t* rsrc = p.route + route_index(req, p.n_layers, p.layer, p.route_heads, g);
+  const uintptr_t rword = reinterpret_cast<uintptr_t>(rsrc) & ~static_cast<uintptr_t>(3);
+  const int32_t* src = lane == 0 ? p.cu_seqlens + req
+                       : lane == 1 ? p.cu_seqlens + req + 1
+                       : lane == 2 ? p.row_ptr + mrow
+                       : lane == 3 ? p.row_ptr + mrow + 1
+                                   : reinterpret_cast<const int32_t*>(rword);
+  const int gv = lane < 5 ? *src : 0;
+  const int tok0 = __builtin_amdgcn_readlane(gv, 0);
+  const int S = __builtin_amdgcn_readlane(gv, 1) - tok0;
+  const int rb = __builtin_amdgcn_readlane(gv, 2), re = __builtin_amdgcn_readlane(gv, 3);
+  const int rbyte = (__builtin_amdgcn_readlane(gv, 4) >> (8 * (reinterpret_cast<uintptr_t>(rsrc) & 3))) & 0xff;
   const int q0 = t * BM;
   if (q0 >= S) return;
-  const bool fa = SOFT || p.route[route_index(req, p.n_layers, p.layer, p.route_heads, g)] != 0;
+  const bool fa = SOFT || rbyte != 0;
+  const int q_end = min(q0 + BM, S);
 
-  __shared__ int32_t cols_raw[TileList<BM, BN>::kLdsCols];
   TileList<BM, BN> tiles;
-  tiles.init(p, t, min(q0 + BM, S), fa, (lds_i32*)(cols_raw), tid, NT);
+  tiles.init(p, t, fa, rb, re, lane);
+  tiles.trim(q_end);
   // SOFT: the SA blocks of this query block, walked in step with the FA tiles
   TileList<BM, BN> sa_tiles;
   int sa_next = 0, sa_blocks = 0;
   if constexpr (SOFT) {
-    __syncthreads();  // the FA list has no LDS columns; the SA list stages its own
-    sa_tiles.init(p, t, min(q0 + BM, S), false, (lds_i32*)(cols_raw), tid, NT);
+    sa_tiles.init(p, t, false, rb, re, lane);
+    sa_tiles.trim(q_end);
     sa_blocks = (sa_tiles.n_tiles + TileList<BM, BN>::TPB - 1) / TileList<BM, BN>::TPB;
   }
   Loader ld;
   ld.init(p.k, p.v, tok0, p.hkv, g, S, tid);
   WaveAttn<D, BN, SOFT ? 2 : 1> wa;
-  wa.init(p.q, tok0, p.hq, head, q0 + wave * 32, S, p.scale, lane);
+  wa.init(p.q, tok0, p.hq, head, q0 + wave * 32, S, p.scale, lane);  // in flight with the first tile
   const int n_tiles = tiles.n_tiles;
   const int n_mine = tiles.visible(q0 + wave * 32, S);
 
@@ -542,7 +579,8 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   auto step = [&](int n, const lds_u8* kc, const lds_u8* vc, lds_u8* kn, lds_u8* vn) {
     int kst_next = 0;
     if (n + 1 < n_tiles) {
-      kst_next = tiles.start(n + 1);
+      // tiles of one mask block are contiguous: look the column up only at a block's first tile
+      kst_next = (n + 1) % TileList<BM, BN>::TPB != 0 ? kst + BN : tiles.start(n + 1);
       ld.issue(false, kst_next, kn);
       ld.issue(true, kst_next, vn);
     }
@@ -582,11 +620,14 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
       step(n + 1, k1, v1, k0, v0);
     }
   }
+  // O goes out through LDS: wave w stages its rows in tile array w (every
+  // wave has passed the loop's last barrier, so no tile is read any more)
+  lds_u8* const stage = wave == 0 ? k0 : wave == 1 ? k1 : wave == 2 ? v0 : v1;
   if constexpr (SOFT) {
     const float r = p.rsoft[static_cast<int64_t>(req) * p.n_layers + p.layer];
-    wa.store(p.out, tok0, p.hq, head, S, r, 1.0f - r);
+    wa.store(p.out, tok0, p.hq, head, S, stage, lane, r, 1.0f - r);
   } else {
-    wa.store(p.out, tok0, p.hq, head, S);
+    wa.store(p.out, tok0, p.hq, head, S, stage, lane);
   }
 }
 
