@@ -459,8 +459,15 @@ struct TileList {
   __device__ __forceinline__ int start(int n) const {
     if (fa) return n * BN;
     const int bi = n / TPB;
-    const int blk = min(max(bi < 64 ? __builtin_amdgcn_readlane(col_lane, bi) : col_idx[rp0 + bi], 0), t);
-    return blk * BM + (n % TPB) * BN;
+    int c;
+    if (bi < 64) {
+      c = __builtin_amdgcn_readlane(col_lane, bi);
+    } else {
+      // made scalar inside the branch, so the wait for this load stays on
+      // this (rare) path and never covers the tile loads in flight
+      c = __builtin_amdgcn_readfirstlane(col_idx[rp0 + bi]);
+    }
+    return min(max(c, 0), t) * BM + (n % TPB) * BN;
   }
   // tiles a wave whose first row is wrow0 must see (up to its last row)
   __device__ __forceinline__ int visible(int wrow0, int S) const {
