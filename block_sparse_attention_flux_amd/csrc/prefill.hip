@@ -539,22 +539,22 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   const int head = g * group + hi;
 
   // Sequence bounds, the mask row's CSR bounds and the route byte: one
-  // gathered load (lane i reads word i), so the workgroup pays a single
-  // memory round trip for all of them.  The route byte comes with the
-  // aligned word that holds it (that word never crosses a page).
+  // gathered load (lanes 0-3 read a word each, lane 4 the byte), so the
+  // workgroup pays a single memory round trip for all of them.
   const int mrow = min(t, p.mask_blocks - 1);
-  const uint8_t* rsrc = p.route + route_index(req, p.n_layers, p.layer, p.route_heads, g);
-  const uintptr_t rword = reinterpret_cast<uintptr_t>(rsrc) & ~static_cast<uintptr_t>(3);
   const int32_t* src = lane == 0 ? p.cu_seqlens + req
                        : lane == 1 ? p.cu_seqlens + req + 1
                        : lane == 2 ? p.row_ptr + mrow
-                       : lane == 3 ? p.row_ptr + mrow + 1
-                                   : reinterpret_cast<const int32_t*>(rword);
-  const int gv = lane < 5 ? *src : 0;
+                                   : p.row_ptr + mrow + 1;
+  int gv = 0;
+  if (lane < 4)
+    gv = *src;
+  else if (lane == 4 && !SOFT)
+    gv = p.route[route_index(req, p.n_layers, p.layer, p.route_heads, g)];
   const int tok0 = __builtin_amdgcn_readlane(gv, 0);
   const int S = __builtin_amdgcn_readlane(gv, 1) - tok0;
   const int rb = __builtin_amdgcn_readlane(gv, 2), re = __builtin_amdgcn_readlane(gv, 3);
-  const int rbyte = (__builtin_amdgcn_readlane(gv, 4) >> (8 * (reinterpret_cast<uintptr_t>(rsrc) & 3))) & 0xff;
+  const int rbyte = __builtin_amdgcn_readlane(gv, 4);
   const int q0 = t * BM;
   if (q0 >= S) return;
   const bool fa = SOFT || rbyte != 0;
