@@ -552,7 +552,7 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   else if (lane == 4 && !SOFT)
     gv = p.route[route_index(req, p.n_layers, p.layer, p.route_heads, g)];
   const int tok0 = __builtin_amdgcn_readlane(gv, 0);
-  const int S = __builtin_amdgcn_readlane(gv, 1) - tok0;
+  const int S = min(__builtin_amdgcn_readlane(gv, 1) - tok0, p.max_seqlen);  // longer requests are cut
   const int rb = __builtin_amdgcn_readlane(gv, 2), re = __builtin_amdgcn_readlane(gv, 3);
   const int rbyte = __builtin_amdgcn_readlane(gv, 4);
   const int q0 = t * BM;

@@ -21,8 +21,11 @@
  * - All arguments are validated on the host before anything is launched; on
  *   failure a negative flux_status is returned and nothing is launched.  Data
  *   that lives on the device (lengths, routes, mask rows) cannot be checked on
- *   the host: kernels clamp it into range so that bad values give wrong
- *   numbers, never out-of-bounds accesses.
+ *   the host: kernels clamp routes, decode lengths and mask columns into
+ *   range so that bad values give wrong numbers, never out-of-bounds
+ *   accesses.  Offsets into other arrays are trusted and must be valid:
+ *   prefill's cu_seqlens (they address the packed tensors) and a mask's
+ *   row_ptr (it addresses col_idx).
  * - A launch failure reported by the HIP runtime returns FLUX_ERR_HIP.
  * - No C++ exception crosses this interface.
  */
@@ -173,12 +176,17 @@ flux_status flux_build_block_mask_dynamic(const uint16_t* q, const uint16_t* k, 
  * Requests never attend to each other.  bf16 in/out, fp32 accumulation.
  *
  * q, out      [device] bf16 [T][hq][head_dim];  k, v [device] bf16 [T][hkv][head_dim]
- * cu_seqlens  [device] int32 [n_req+1];  max_seqlen [host] >= every request length
+ * cu_seqlens  [device] int32 [n_req+1], non-decreasing, cu_seqlens[n_req] = T
+ *             (the kernels trust the offsets: they address q/k/v/out with
+ *             them; a length above max_seqlen is cut to max_seqlen rows)
+ * max_seqlen  [host] >= every request length
  * softmax_scale  > 0 (usually 1/sqrt(head_dim))
- * route       [device] uint8 [n_req][n_layers], read at [r][layer]; 1 = FA
+ * route       [device] uint8 [n_req][n_layers], read at [r][layer]; nonzero = FA
  * mask_row_ptr, mask_col_idx  [device] CSR of flux_build_block_mask for
  *             mask_blocks >= ceil(max_seqlen / block_size) rows; columns must
- *             be increasing within a row.  Only read by SA layers.
+ *             be increasing within a row (columns past a row's diagonal are
+ *             clamped to it).  Every workgroup reads its row's bounds; only SA
+ *             layers read the columns.
  * Supported: head_dim in {64, 128}, block_size in {64, 128}, hq % hkv == 0,
  *            hq / hkv <= 16.  out may not alias q, k or v.
  */
