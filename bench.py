@@ -612,16 +612,23 @@ def run_decode(args, flux, syn, dev, stream, log):
         step()
     torch.cuda.synchronize()
     log(f"decode timed x{args.decode_steps}")
-    per_step = []
+    # whole steps back to back, events only around them
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.decode_steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / args.decode_steps
+    # the per-layer split (FA vs SA layer times) from separate steps with an
+    # event between layers
     lay = np.zeros(nl)
     for _ in range(args.decode_steps):
         tm = []
         step(tm)
         torch.cuda.synchronize()
-        per_step.append(tm[0].elapsed_time(tm[-1]))
         lay += np.array([tm[i].elapsed_time(tm[i + 1]) for i in range(nl)])
     lay /= args.decode_steps
-    step_ms = float(np.mean(per_step))
 
     # The same step captured once in a HIP graph and replayed: the host's
     # launch gaps between the 72 kernels disappear.  Every checked replay must
@@ -637,7 +644,6 @@ def run_decode(args, flux, syn, dev, stream, log):
         torch.cuda.synchronize()
         if not all(torch.equal(a, b) for a, b in zip(out, eager)):
             raise RuntimeError("decode graph replay differs from the eager step")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.decode_steps):
         graph.replay()
