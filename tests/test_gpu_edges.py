@@ -146,3 +146,21 @@ def test_softmax_scales(scale):
         torch.cuda.synchronize()
         ref = oracle.attention_decode(f32(qd), f32(kc), f32(vc), [600, 65], layer == 0, m, B, scale)
         assert_attn_close(f32(out), ref, f"decode scale {scale} layer {layer}")
+
+
+def test_request_longer_than_max_seqlen_is_cut():
+    """A request longer than max_seqlen is cut to max_seqlen rows: those rows
+    are exact (a causal row never reads keys past itself) and the rows past
+    the cut are left untouched."""
+    say("request longer than max_seqlen")
+    lens, hq, hkv, d, B, cut = [300], 4, 2, 128, 64, 200
+    route_rows = [[1, 0]]
+    q, k, v, cu, sa, rp, ci, route = run_prefill_case(lens, hq, hkv, d, B, 1, 2, route_rows, 91)
+    m = oracle.block_mask(oracle.num_blocks(max(lens), B), 1, 2)
+    for layer in (0, 1):
+        out = torch.full_like(q, float("nan"))
+        flux.attn_prefill(q, k, v, cu, cut, route, layer, rp, ci, sa, out=out)
+        torch.cuda.synchronize()
+        assert torch.isnan(out[cut:]).all()
+        ref = oracle.attention_prefill(f32(q)[:cut], f32(k)[:cut], f32(v)[:cut], layer == 0, m, B)
+        assert_attn_close(f32(out)[:cut], ref, f"cut layer {layer}")
