@@ -65,7 +65,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path would shard by KV-head group or by sequence, see DESIGN.md)", file=sys.stderr)
+              "(the path would shard by KV-head group for prefill and by sequence for decode)", file=sys.stderr)
         return 2
 
     import numpy as np

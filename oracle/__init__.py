@@ -15,11 +15,11 @@ What it computes, and where the pages define it
 * ``mask``      -- block mask of the Sparse Attention layers: sink blocks plus
   a causal local window of blocks (the pages name block-sparse attention via
   the Block-Sparse-Attention library on the Qwen3-4B model card, "Sample
-  Usage"; the sink+window pattern is a reading).
+  Usage"; the sink+window pattern is a reading of them).
 * ``dynmask``   -- a content-aware block mask (mean-pooled coarse attention,
   Top-tau selection); the pages only hint at it (model card slug, "Daily
   Papers" page: Prism and RRAttention abstracts), so the definition is a
-  reading, see the design doc.
+  reading of those abstracts.
 * ``attention`` -- the plain masked-softmax definition
   ``O = softmax(Q K^T / sqrt(d) + mask) V`` with grouped KV heads, for prefill
   and for one-token decode that reuses the prefill route (technical summary,

@@ -7,7 +7,7 @@ encoder, and decides per layer between Full Attention (FA) and Sparse
 Attention (SA).  At inference the soft routing weight is thresholded to a
 deterministic 0/1 (same section, "switch to hard routing").
 
-Readings where the pages leave a step open (all listed in the design doc):
+Readings where the pages leave a step open:
 * pooling operator = arithmetic mean over the SET of pooled positions (a row
   that is both among the first and the last 100 counts once);
 * MLP = Linear(D->H1) -> ReLU -> Linear(H1->L), weights in PyTorch
