@@ -302,21 +302,46 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   }
 }
 
-// Merge the nsplit partials of one (sequence, head): one thread per d.
+// Merge the nsplit partials of one (sequence, head): one thread per d.  Up
+// to kCombineBatch splits are read with all their loads in flight together
+// (one memory round trip); the sum runs over the splits in order either way.
+constexpr int kCombineBatch = 16;
+
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p) {
   const int sh = blockIdx.x;  // b * hq + head
   const int dd = threadIdx.x;
-  const float* ml = p.part_ml + static_cast<size_t>(sh) * p.nsplit * 2;
-  const float* po = p.part_o + static_cast<size_t>(sh) * p.nsplit * D;
-  float m = kNegInf;
-  for (int s = 0; s < p.nsplit; ++s) m = fmaxf(m, ml[s * 2]);
-  float o = 0.0f, l = 0.0f;
-  for (int s = 0; s < p.nsplit; ++s) {
-    const float ms = ml[s * 2];
-    const float sc = (ms == kNegInf) ? 0.0f : fast_exp2(ms - m);
-    o += sc * po[static_cast<size_t>(s) * D + dd];
-    l += sc * ml[s * 2 + 1];
+  const int ns = p.nsplit;
+  const float* ml = p.part_ml + static_cast<size_t>(sh) * ns * 2;
+  const float* po = p.part_o + static_cast<size_t>(sh) * ns * D;
+  float m = kNegInf, o = 0.0f, l = 0.0f;
+  if (ns <= kCombineBatch) {
+    float mv[kCombineBatch], lv[kCombineBatch], ov[kCombineBatch];
+#pragma unroll
+    for (int s = 0; s < kCombineBatch; ++s) {
+      const bool ok = s < ns;
+      mv[s] = ok ? ml[s * 2] : kNegInf;
+      lv[s] = ok ? ml[s * 2 + 1] : 0.0f;
+      ov[s] = ok ? po[static_cast<size_t>(s) * D + dd] : 0.0f;
+    }
+#pragma unroll
+    for (int s = 0; s < kCombineBatch; ++s) m = fmaxf(m, mv[s]);
+#pragma unroll
+    for (int s = 0; s < kCombineBatch; ++s) {
+      if (s < ns) {
+        const float sc = (mv[s] == kNegInf) ? 0.0f : fast_exp2(mv[s] - m);
+        o += sc * ov[s];
+        l += sc * lv[s];
+      }
+    }
+  } else {
+    for (int s = 0; s < ns; ++s) m = fmaxf(m, ml[s * 2]);
+    for (int s = 0; s < ns; ++s) {
+      const float ms = ml[s * 2];
+      const float sc = (ms == kNegInf) ? 0.0f : fast_exp2(ms - m);
+      o += sc * po[static_cast<size_t>(s) * D + dd];
+      l += sc * ml[s * 2 + 1];
+    }
   }
   const float val = l > 0.0f ? o / l : 0.0f;
   p.out[static_cast<size_t>(sh) * D + dd] = static_cast<uint16_t>(pack_bf16x2(val, 0.0f) & 0xffffu);
