@@ -65,19 +65,28 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   const int b = unit / p.hkv, g = unit % p.hkv;
   const int group = p.hq / p.hkv;
 
-  const int N = min(max(p.seqlens[b], 1), p.max_len);
+  // The sequence length and the route byte do not depend on each other and
+  // are read together; only an SA layer then reads its mask row (bounds, then
+  // the first 64 columns, lane i keeping column i), so an FA layer's first
+  // K/V loads wait on one round trip and an SA layer's on three.
+  // (one gathered load: lane 0 the length, lane 1 the route byte; a compact
+  // cache only holds an SA layer's rows and comes without a route)
+  int gv = 0;
+  if (lane == 0)
+    gv = p.seqlens[b];
+  else if (lane == 1 && !p.compact)
+    gv = p.route[route_index(b, p.n_layers, p.layer, p.route_heads, g)];
+  const int n_raw = __builtin_amdgcn_readlane(gv, 0);
+  const bool fa = !p.compact && __builtin_amdgcn_readlane(gv, 1) != 0;
+  const int N = min(max(n_raw, 1), p.max_len);
   const int B = p.block_size;
   const int mrow = min((N - 1) / B, p.mask_blocks - 1);
-  // The route, the mask row's bounds and its first 64 columns are read
-  // together, before the layer type is known (the mask is always present),
-  // so an SA layer's first K/V loads wait on one round trip, not three.
-  // Lane i keeps column i of the row.
-  const int rp0 = p.row_ptr[mrow];
-  const int n_blk = max(p.row_ptr[mrow + 1] - rp0, 0);
-  // a compact cache only holds an SA layer's rows (and comes without a route)
-  bool fa = false;
-  if (!p.compact) fa = p.route[route_index(b, p.n_layers, p.layer, p.route_heads, g)] != 0;
-  const int col_lane = lane < n_blk ? min(max(p.col_idx[rp0 + lane], 0), mrow) : 0;
+  int rp0 = 0, n_blk = 0, col_lane = 0;
+  if (!fa) {
+    rp0 = p.row_ptr[mrow];
+    n_blk = max(p.row_ptr[mrow + 1] - rp0, 0);
+    col_lane = lane < n_blk ? min(max(p.col_idx[rp0 + lane], 0), mrow) : 0;
+  }
   const int U = fa ? N : n_blk * B;
   // contiguous range of visited-key indices for this split, chunk aligned
   const int per = ((U + p.nsplit - 1) / p.nsplit + kChunk - 1) / kChunk * kChunk;
