@@ -164,3 +164,30 @@ def test_request_longer_than_max_seqlen_is_cut():
         assert torch.isnan(out[cut:]).all()
         ref = oracle.attention_prefill(f32(q)[:cut], f32(k)[:cut], f32(v)[:cut], layer == 0, m, B)
         assert_attn_close(f32(out)[:cut], ref, f"cut layer {layer}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(6, 2), (5, 1), (7, 7)])
+def test_odd_gqa_groups(hq, hkv):
+    """GQA groups of 3, 5 and 1 query heads per kv head: prefill (both layer
+    types, ragged lengths) and decode against the oracle."""
+    say(f"odd GQA group hq={hq} hkv={hkv}")
+    lens, d, B = [333, 70, 129], 128, 64
+    route_rows = [[1, 0], [0, 1], [1, 1]]
+    q, k, v, cu, sa, rp, ci, route = run_prefill_case(lens, hq, hkv, d, B, 1, 2, route_rows, 95 + hq)
+    m = oracle.block_mask(oracle.num_blocks(max(lens), B), 1, 2)
+    cu_h = np.cumsum([0] + lens)
+    for layer in (0, 1):
+        out = flux.attn_prefill(q, k, v, cu, max(lens), route, layer, rp, ci, sa)
+        torch.cuda.synchronize()
+        check_varlen(q, k, v, cu_h, lens, route_rows, layer, out, m, B, what=f"group {hq // hkv}")
+    seqlens = [333, 64, 1]
+    qd, kc, vc, sl = make_decode(3, 333, seqlens, hq, hkv, d, 96 + hq)
+    _, rp2, ci2 = flux.build_block_mask(333, sa, dense=False)
+    rt = torch.tensor(route_rows, dtype=torch.uint8, device=DEV)
+    for layer in (0, 1):
+        out = flux.attn_decode(qd, kc, vc, sl, rt, layer, rp2, ci2, sa)
+        torch.cuda.synchronize()
+        for i, n in enumerate(seqlens):
+            ref = oracle.attention_decode(f32(qd[i:i + 1]), f32(kc[i:i + 1]), f32(vc[i:i + 1]), [n],
+                                          route_rows[i][layer] == 1, m, B)
+            assert_attn_close(f32(out[i:i + 1]), ref, f"decode group {hq // hkv} seq {i} layer {layer}")
