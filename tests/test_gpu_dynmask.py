@@ -102,6 +102,8 @@ def qk(S, hq, hkv, d, seed, planted=False):
     (777, 4, 4, 64, 64, 0.9, 2, 6, False),
     (2048, 16, 2, 128, 128, 0.5, 0, 0, True),
     (1300, 8, 1, 64, 64, 0.3, 1, 4, True),
+    (640, 6, 2, 64, 64, 0.7, 1, 0, False),     # group 3 (padded to 4 in the kernel)
+    (900, 16, 1, 128, 64, 0.8, 2, 6, True),    # group 16
 ])
 def test_dynamic_mask_matches_oracle(case):
     S, hq, hkv, d, B, tau, sink, cap, planted = case
