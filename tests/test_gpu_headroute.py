@@ -27,6 +27,7 @@ DEV = "cuda"
     # lens, hq, hkv, d, B, s, w
     ([700, 1, 2100, 129], 8, 4, 128, 128, 1, 3),
     ([1500, 333], 16, 8, 64, 64, 2, 4),
+    ([900, 257], 6, 2, 128, 128, 1, 2),    # group 3
 ])
 def test_prefill_head_route(case):
     lens, hq, hkv, d, B, s, w = case
