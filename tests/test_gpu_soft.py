@@ -25,6 +25,7 @@ DEV = "cuda"
     # lens, hq, hkv, d, B, s, w, r per request
     ([900, 1, 2300, 130], 8, 2, 128, 128, 1, 3, [0.3, 1.0, 0.0, 0.8]),
     ([1024, 515], 4, 4, 64, 64, 2, 2, [0.5, 0.125]),
+    ([700, 260], 6, 2, 64, 128, 1, 2, [0.7, 0.2]),    # group 3, d 64 with 128-row blocks
 ])
 def test_soft_prefill(case):
     lens, hq, hkv, d, B, s, w, rs = case
