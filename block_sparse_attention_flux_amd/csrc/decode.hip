@@ -270,14 +270,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   float* mo = reinterpret_cast<float*>(lds);            // [wave][16 q][D]
   float* mm = mo + kWaves * 16 * D;                     // [wave][16] max
   float* ml = mm + kWaves * 16;                         // [wave][16] sum
+  if (l16 < group) {  // the padding columns of the MFMA tile are never read
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      mo[(wave * 16 + l16) * D + dt * 16 + quarter * 4 + r] = oacc[dt][r];
-  if (quarter == 0) {
-    mm[wave * 16 + l16] = m_run;
-    ml[wave * 16 + l16] = lsum;
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4*>(mo + (wave * 16 + l16) * D + dt * 16 + quarter * 4) = oacc[dt];
+    if (quarter == 0) {
+      mm[wave * 16 + l16] = m_run;
+      ml[wave * 16 + l16] = lsum;
+    }
   }
   __syncthreads();
 
