@@ -417,7 +417,8 @@ struct WaveAttn {
     for (int i = 0; i < 32 / RPI; ++i) {
       const int r = RPI * i + lane / CH, chunk = lane % CH;
       const u32x4 v = *reinterpret_cast<const lds_u32x4*>(stage + r * (D * 2) + ((chunk ^ swz(r)) * 16));
-      if (wrow0 + r < S) st16(out + (static_cast<size_t>(tok0 + wrow0 + r) * hq + head) * D + chunk * 8, v);
+      if (wrow0 + r < S)  // streaming store: this kernel never reads O back
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + (static_cast<size_t>(tok0 + wrow0 + r) * hq + head) * D + chunk * 8));
     }
   }
 };
