@@ -383,7 +383,7 @@ def attainable(flux, dev, stream, log):
     log(f"attainable: bf16 MFMA loop {mfma_tflops:.0f} TF/s, HBM streaming read {read_gbs:.0f} GB/s")
     return {"mfma_tflops": round(mfma_tflops, 1), "hbm_read_gbs": round(read_gbs, 1),
             "how": "library probe kernels: 768 workgroups x 4 waves of v_mfma_f32_32x32x16_bf16 chains; "
-                   "one read of a 2 GiB buffer with 16-byte loads; best of 3"}
+                   "one read of a 2 GiB buffer with 16-byte streaming loads; best of 3"}
 
 
 def counted_traffic(kernel):

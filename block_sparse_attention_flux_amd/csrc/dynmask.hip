@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const uint16_t* __restri
   float acc[8] = {};
 #pragma unroll 4
   for (int r = r0 + rl; r < r1; r += RL) {
-    const u32x4 v = ld16(src + (static_cast<size_t>(r) * H + h) * D + c * 8);
+    const u32x4 v = ld16_stream(src + (static_cast<size_t>(r) * H + h) * D + c * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc[2 * e] += bf16_bits_to_f32(static_cast<uint16_t>(v[e] & 0xffffu));

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict
   for (size_t i = static_cast<size_t>(blockIdx.x) * 256 * 4 + threadIdx.x; i < n16; i += stride) {
     u32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = (i + u * 256 < n16) ? src[i + u * 256] : u32x4{0, 0, 0, 0};
+    for (int u = 0; u < 4; ++u) v[u] = (i + u * 256 < n16) ? ld16_stream(src + i + u * 256) : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }

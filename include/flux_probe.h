@@ -24,8 +24,9 @@ extern "C" {
 int32_t flux_probe_mfma(float* sink, int32_t n_workgroups, int32_t iters, void* stream);
 double flux_probe_mfma_flops(int32_t n_workgroups, int32_t iters);
 
-/* Reads `bytes` (a multiple of 16) at src [device] once with 16-byte loads;
- * sink [device] uint32 [n_workgroups] receives one word per workgroup. */
+/* Reads `bytes` (a multiple of 16) at src [device] once with 16-byte
+ * streaming (non-temporal) loads, the form the decode kernel reads its caches
+ * with; sink [device] uint32 [n_workgroups] receives one word per workgroup. */
 int32_t flux_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t n_workgroups,
                         void* stream);
 
