@@ -386,17 +386,31 @@ def attainable(flux, dev, stream, log):
                    "one read of a 2 GiB buffer with 16-byte streaming loads; best of 3"}
 
 
+def build_flags(source):
+    """The extra hipcc flags the package's build script gives `source`."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_flux_build", os.path.join(ROOT, "block_sparse_attention_flux_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return list(mod.EXTRA_FLAGS.get(os.path.basename(source), []))
+
+
 def counted_traffic(kernel):
     """HBM bytes measured by rocprofv3 counters for `kernel`, or None once the
-    kernel's source has changed since the counters were taken."""
+    kernel's source or its build flags have changed since the counters were
+    taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic_32k.json")
     try:
         rec = json.load(open(path))[kernel]
         src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        flags = build_flags(rec["source"])
     except (OSError, KeyError, ValueError):
         return None
-    return rec if hashlib.sha256(src).hexdigest() == rec["source_sha256"] else None
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"] or rec.get("build_flags", []) != flags:
+        return None
+    return rec
 
 
 def _events(torch, stream, n):

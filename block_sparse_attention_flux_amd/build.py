@@ -30,6 +30,13 @@ HIPCC_FLAGS = [
 ]
 
 
+# Extra flags per source.  prefill.hip: LLVM's iterative scheduler in its ILP
+# mode (each region scheduled for instruction-level parallelism, kept only
+# where the kernel's occupancy still holds); measured on the 32K layers at the
+# same occupancy: ~1 % faster FA, ~0.5 % SA, bit-identical results.
+EXTRA_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+
+
 def hipcc():
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(exe):
@@ -44,7 +51,8 @@ def sources():
 
 def _compile(src):
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj]
+    extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n{r.stderr}")

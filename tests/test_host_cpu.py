@@ -93,10 +93,22 @@ def test_counted_traffic_follows_the_source_hash(tmp_path, monkeypatch):
     src.write_text("kernel source v1\n")
     (tmp_path / "profiles").mkdir()
     rec = {"source": "k.hip", "source_sha256": hashlib.sha256(b"kernel source v1\n").hexdigest(),
-           "fa_bytes": 123}
+           "build_flags": ["-O9"], "fa_bytes": 123}
     (tmp_path / "profiles" / "hbm_traffic_32k.json").write_text(json.dumps({"k": rec}))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "build_flags", lambda source: ["-O9"])
     assert bench.counted_traffic("k")["fa_bytes"] == 123
     assert bench.counted_traffic("other") is None
+    monkeypatch.setattr(bench, "build_flags", lambda source: [])  # built differently since
+    assert bench.counted_traffic("k") is None
+    monkeypatch.setattr(bench, "build_flags", lambda source: ["-O9"])
     src.write_text("kernel source v2\n")  # the kernel changed since the counters were taken
     assert bench.counted_traffic("k") is None
+
+
+def test_build_flags_of_the_package_sources():
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.build_flags("block_sparse_attention_flux_amd/csrc/prefill.hip") == \
+        ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+    assert bench.build_flags("block_sparse_attention_flux_amd/csrc/decode.hip") == []
