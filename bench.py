@@ -71,10 +71,8 @@ def main():
     import numpy as np
     import torch
 
-    lib = os.path.join(ROOT, "block_sparse_attention_flux_amd", "lib", "libflux.so")
-    if not os.path.exists(lib):
-        import __graft_entry__
-        __graft_entry__.build()
+    import __graft_entry__
+    __graft_entry__._build_module().ensure_built()  # rebuilds only if the sources changed
     import block_sparse_attention_flux_amd as flux
     from synth import inputs as syn
 
@@ -563,17 +561,9 @@ def run_varlen8(flux, syn, dev, stream, log):
     e1.record(stream)
     torch.cuda.synchronize()
     dec_ms = e0.elapsed_time(e1) / wl.decode_steps
-    # bytes per step: every visited K/V row once (FA: the whole cache, SA: sink + window rows)
-    row_b = wl.hkv * d * 2 * 2
-    byts = 0
-    for i, S in enumerate(lens):
-        for layer in range(L):
-            N = S + wl.decode_steps // 2
-            if r[i, layer]:
-                byts += N * row_b
-            else:
-                mrow = (N - 1) // wl.block_size
-                byts += min(mrow + 1, wl.sink_blocks + wl.local_blocks) * wl.block_size * row_b
+    # bytes per step, averaged over the steps: every K/V row the step reads,
+    # once (FA: the N cached keys; SA: the keys below N of its mask row's blocks)
+    byts = decode_bytes_varlen(lens, r, wl, range(1, wl.decode_steps + 1)) / wl.decode_steps
     res = {"workload": "Llama-3-8B-shaped varlen mix: 8 prompts (seeded lengths in [8192, 65536]), "
                        "32 layers routed per request by the router (4096->256->32), then 128 decode steps",
            "lengths": lens, "fa_layers_per_request": r.sum(axis=1).tolist(),
@@ -581,12 +571,31 @@ def run_varlen8(flux, syn, dev, stream, log):
            "prefill_tflops": round(flops / pre_ms / 1e9, 1),
            "decode_ms_per_step": round(dec_ms, 4), "decode_tok_s": round(n / (dec_ms * 1e-3), 1),
            "decode_gbs": round(byts / (dec_ms * 1e-3) / 1e9, 1),
-           "decode_note": "step time includes the per-layer K/V row append (flux_kv_append); bytes at "
-                          "the mid-point cache length"}
+           "decode_note": "step time includes the per-layer K/V row append (flux_kv_append); bytes are "
+                          "the K/V rows each step reads at its own cache length, averaged over the 128 steps"}
     log(f"varlen8 decode: {dec_ms:.3f} ms/step ({res['decode_tok_s']:.0f} tok/s, {res['decode_gbs']:.0f} GB/s)")
     del kc, vc, knew, vnew, qd
     torch.cuda.empty_cache()
     return res
+
+
+def decode_bytes_varlen(lens, route, wl, grow):
+    """K/V bytes that decode steps read: for every step (cache length
+    lens[i] + t for t in grow), request and layer, the rows of the keys the
+    layer visits (FA: all N keys; SA: the keys below N of mask row (N-1)/B,
+    i.e. its sink blocks and window blocks, the last one partial)."""
+    B, s, w = wl.block_size, wl.sink_blocks, wl.local_blocks
+    row_b = wl.hkv * wl.head_dim * 2 * 2
+    total = 0
+    for i, S in enumerate(lens):
+        n_fa = int(route[i].sum())
+        for t in grow:
+            N = S + t
+            mrow = (N - 1) // B
+            blocks = min(mrow + 1, w) + min(s, max(0, mrow + 1 - w))
+            sa_keys = (blocks - 1) * B + (N - mrow * B)
+            total += (n_fa * N + (len(route[i]) - n_fa) * sa_keys) * row_b
+    return total
 
 
 def run_decode(args, flux, syn, dev, stream, log):

@@ -224,8 +224,9 @@ def decode_workspace_size(n_seq, hq, hkv, head_dim, max_len):
 
 
 def decode_workspace(n_seq, hq, hkv, head_dim, max_len, device="cuda"):
-    """A device buffer of flux_attn_decode_workspace_size bytes (zero-filled)."""
-    return torch.zeros(max(decode_workspace_size(n_seq, hq, hkv, head_dim, max_len), 1),
+    """A device buffer of flux_attn_decode_workspace_size bytes (its contents
+    do not matter; torch's allocations are 16-byte aligned)."""
+    return torch.empty(max(decode_workspace_size(n_seq, hq, hkv, head_dim, max_len), 16),
                        dtype=torch.uint8, device=device)
 
 

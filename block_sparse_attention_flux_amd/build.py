@@ -4,10 +4,14 @@
 
 (Run it as a file: importing the package itself loads the built library.)
 
-The library lands at ``block_sparse_attention_flux_amd/lib/libflux.so``.
+The library lands at ``block_sparse_attention_flux_amd/lib/libflux.so``, with
+``libflux.stamp`` beside it: the sha256 of every source, header and build
+flag it was built from.  ensure_built() rebuilds whenever that stamp does not
+match the tree, so nothing runs against a library built from other sources.
 """
 
 import concurrent.futures
+import hashlib
 import os
 import shutil
 import subprocess
@@ -59,10 +63,46 @@ def _compile(src):
     return obj
 
 
+STAMP = os.path.join(OUT_DIR, "libflux.stamp")
+
+
+def source_digest():
+    """sha256 over the sources, the public headers and the build flags."""
+    h = hashlib.sha256()
+    files = sources() + sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h"))
+    files += sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
+    for path in files:
+        h.update(os.path.relpath(path, ROOT).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    h.update(repr((HIPCC_FLAGS, sorted(EXTRA_FLAGS.items()))).encode())
+    return h.hexdigest()
+
+
+def is_current():
+    out = os.path.join(OUT_DIR, LIB_NAME)
+    try:
+        with open(STAMP) as f:
+            return os.path.exists(out) and f.read().strip() == source_digest()
+    except OSError:
+        return False
+
+
+def ensure_built():
+    """Build unless libflux.so exists and its stamp matches the current tree."""
+    out = os.path.join(OUT_DIR, LIB_NAME)
+    if is_current():
+        return out
+    why = "not built" if not os.path.exists(out) else "built from other sources"
+    print(f"[flux build] libflux.so {why}: building", file=sys.stderr, flush=True)
+    return build()
+
+
 def build(verbose=False):
     """Compile every source and link libflux.so; always rebuilds."""
     os.makedirs(OBJ_DIR, exist_ok=True)
     os.makedirs(OUT_DIR, exist_ok=True)
+    digest = source_digest()  # of the tree the objects are compiled from
     srcs = sources()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
@@ -73,6 +113,8 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, out)
+    with open(STAMP, "w") as f:
+        f.write(digest + "\n")
     if verbose:
         print(f"built {out}")
     return out

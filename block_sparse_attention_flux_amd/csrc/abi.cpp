@@ -76,6 +76,28 @@ flux_status attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
   return from_hip(flux::launch_prefill(pp, static_cast<hipStream_t>(stream)));
 }
 
+// Work-item shape and workspace pointers of a decode call.  The workspace is
+// needed (and checked) only when a call can have more items than units.
+flux_status decode_layout(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_dim, int32_t max_len,
+                          void* workspace, size_t workspace_bytes, flux::DecodeParams* dp) {
+  const flux::DecodeShape sh = flux::decode_shape(n_seq, hkv, max_len);
+  if (sh.slots > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
+  const int64_t units = static_cast<int64_t>(n_seq) * hkv;
+  const bool partials = sh.slots > units;
+  const size_t need = flux::decode_workspace_bytes(n_seq, hq, hkv, head_dim, max_len);
+  if (partials && (workspace == nullptr || workspace_bytes < need ||
+                   reinterpret_cast<uintptr_t>(workspace) % 16 != 0))
+    return FLUX_ERR_WORKSPACE;
+  const size_t n_part = static_cast<size_t>(sh.slots) * (hq / hkv);
+  float* ws = partials ? static_cast<float*>(workspace) : nullptr;
+  dp->part_o = ws;
+  dp->part_ml = ws != nullptr ? ws + n_part * head_dim : nullptr;
+  dp->plan = ws != nullptr ? reinterpret_cast<int2*>(ws + n_part * (head_dim + 2)) : nullptr;
+  dp->slots = static_cast<int32_t>(sh.slots);
+  dp->balanced = sh.balanced;
+  return FLUX_OK;
+}
+
 flux_status attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                         uint16_t* out, const int32_t* seqlens, int32_t n_seq, int32_t max_len,
                         int32_t hq, int32_t hkv, int32_t head_dim, float softmax_scale,
@@ -91,19 +113,15 @@ flux_status attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16
   const flux_status st = check_attn_common(hq, hkv, head_dim, softmax_scale, route, n_layers, layer,
                                            mask_row_ptr, mask_col_idx, mask_blocks, max_len, p);
   if (st != FLUX_OK) return st;
-  const int32_t ns = flux::decode_splits(n_seq, hkv, max_len);
-  if (static_cast<int64_t>(n_seq) * hkv * ns > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
-  const size_t need = flux_attn_decode_workspace_size(n_seq, hq, hkv, head_dim, max_len);
-  if (ns > 1 && (workspace == nullptr || workspace_bytes < need)) return FLUX_ERR_WORKSPACE;
   flux::DecodeParams dp{};
+  const flux_status ws = decode_layout(n_seq, hq, hkv, head_dim, max_len, workspace,
+                                       workspace_bytes, &dp);
+  if (ws != FLUX_OK) return ws;
   dp.q = q; dp.k_cache = k_cache; dp.v_cache = v_cache; dp.out = out;
   dp.seqlens = seqlens; dp.route = route; dp.row_ptr = mask_row_ptr; dp.col_idx = mask_col_idx;
-  const size_t slots = static_cast<size_t>(n_seq) * hq * ns;
-  dp.part_o = static_cast<float*>(workspace);
-  dp.part_ml = workspace != nullptr ? static_cast<float*>(workspace) + slots * head_dim : nullptr;
   dp.n_seq = n_seq; dp.max_len = max_len; dp.hq = hq; dp.hkv = hkv; dp.head_dim = head_dim;
   dp.n_layers = n_layers; dp.layer = layer; dp.mask_blocks = mask_blocks;
-  dp.block_size = p.block_size; dp.nsplit = ns; dp.scale = softmax_scale;
+  dp.block_size = p.block_size; dp.scale = softmax_scale;
   dp.cache_rows = max_len; dp.compact = 0; dp.route_heads = route_heads;
   dp.sink_blocks = p.sink_blocks; dp.local_blocks = p.local_blocks;
   return from_hip(flux::launch_decode(dp, static_cast<hipStream_t>(stream)));
@@ -263,9 +281,8 @@ flux_status flux_attn_prefill_soft(const uint16_t* q, const uint16_t* k, const u
 size_t flux_attn_decode_workspace_size(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_dim,
                                        int32_t max_len) {
   if (n_seq < 1 || hq < 1 || hkv < 1 || head_dim < 1 || max_len < 1) return 0;
-  const size_t ns = static_cast<size_t>(flux::decode_splits(n_seq, hkv, max_len));
-  const size_t slots = static_cast<size_t>(n_seq) * hq * ns;
-  return slots * (static_cast<size_t>(head_dim) + 2) * sizeof(float);
+  if (hq % hkv != 0) return 0;
+  return flux::decode_workspace_bytes(n_seq, hq, hkv, head_dim, max_len);
 }
 
 flux_status flux_attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
@@ -356,19 +373,15 @@ flux_status flux_attn_decode_sa_compact(const uint16_t* q, const uint16_t* k_cac
   int32_t rows = 0;
   const flux_status sc = check_cache(hkv, head_dim, max_len, 1, p, &rows);
   if (sc != FLUX_OK) return sc;
-  const int32_t ns = flux::decode_splits(n_seq, hkv, max_len);
-  if (static_cast<int64_t>(n_seq) * hkv * ns > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
-  const size_t need = flux_attn_decode_workspace_size(n_seq, hq, hkv, head_dim, max_len);
-  if (ns > 1 && (workspace == nullptr || workspace_bytes < need)) return FLUX_ERR_WORKSPACE;
   flux::DecodeParams dp{};
+  const flux_status ws = decode_layout(n_seq, hq, hkv, head_dim, max_len, workspace,
+                                       workspace_bytes, &dp);
+  if (ws != FLUX_OK) return ws;
   dp.q = q; dp.k_cache = k_cache; dp.v_cache = v_cache; dp.out = out;
   dp.seqlens = seqlens; dp.route = nullptr; dp.row_ptr = mask_row_ptr; dp.col_idx = mask_col_idx;
-  const size_t slots = static_cast<size_t>(n_seq) * hq * ns;
-  dp.part_o = static_cast<float*>(workspace);
-  dp.part_ml = workspace != nullptr ? static_cast<float*>(workspace) + slots * head_dim : nullptr;
   dp.n_seq = n_seq; dp.max_len = max_len; dp.hq = hq; dp.hkv = hkv; dp.head_dim = head_dim;
   dp.n_layers = 1; dp.layer = 0; dp.mask_blocks = mask_blocks;
-  dp.block_size = p.block_size; dp.nsplit = ns; dp.scale = softmax_scale;
+  dp.block_size = p.block_size; dp.scale = softmax_scale;
   dp.cache_rows = rows; dp.compact = 1; dp.route_heads = 1;
   dp.sink_blocks = p.sink_blocks; dp.local_blocks = p.local_blocks;
   return from_hip(flux::launch_decode(dp, static_cast<hipStream_t>(stream)));

@@ -6,9 +6,14 @@
 // section 2, deployment paragraph).  Decode is bound by HBM bandwidth, so the
 // design streams K/V rows once, for all query heads of a GQA group at a time:
 //
-//   grid      = (sequence, kv head, split); the keys a layer must visit (all
-//               N keys for FA, the mask row's blocks for SA) are cut into
-//               `nsplit` contiguous ranges of 32-key chunks;
+//   work list = every (sequence, kv head) unit visits U keys (all N keys for
+//               FA, the mask row's blocks for SA); the units are cut into
+//               work items of about the same number of keys (1024 items for
+//               equal units, at least 256 keys each), so a long FA sequence
+//               beside short SA ones gets proportionally more items.  Each
+//               workgroup plans the whole call itself (every unit's U, its
+//               share of the items, one block-wide prefix sum) and takes item
+//               blockIdx.x: the plan costs no extra launch;
 //   each wave streams its own chunks: K rows go straight from HBM into the A
 //               operand of v_mfma_f32_16x16x32_bf16 (S^T = K Q^T, the group's
 //               query heads padded to 16 columns), V rows are transposed
@@ -26,6 +31,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kChunk = 32;                  // keys per wave iteration
+constexpr int kPlanPerThread = kDecodePlanUnits / (kWaves * 64);  // units per thread in the plan
+static_assert(kPlanPerThread * kWaves * 64 == kDecodePlanUnits, "plan units must fill the workgroup");
 constexpr float kRescaleSlack = 8.0f;       // log2 units the stale max may lag
 constexpr int kVtPitch = kChunk * 2 + 16;   // bytes per V^T row in LDS
 
@@ -45,6 +52,196 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// One work item: keys [u0, u1) of the visited-key list of unit (b, g), item
+// j of the unit's s items (all values wave-uniform).
+struct DecodeItem {
+  int b, g, j, s, N, fa, mrow, rp0, n_blk, u0, u1;
+};
+
+// The unit's length, route and mask row, clamped into range: N in
+// [1, max_len], columns at most the row's own, at most mrow + 1 blocks.
+struct UnitKeys {
+  int N, fa, mrow, rp0, n_blk, U;
+};
+
+// Balanced plan, computed by every workgroup for the whole call.  Thread t
+// owns units [4t, 4t + 4) (unit u = b * hkv + g).  With `total` the keys of
+// all units and T = ceil(total / (1024 - n_units / 2)), unit u gets
+//   s_u = max(1, min(ceil(U_u / T), floor(U_u / 256)))
+// items of about U_u / s_u <= T keys each (chunk aligned), in consecutive
+// slots after those of the units before it: every item holds about the same
+// number of keys, and a call of equal units has exactly 1024 items (two
+// rounds of the 512 workgroups the GPU holds at once).  Returns false when no
+// unit owns item blockIdx.x.  Workgroup 0 also records (first slot, items)
+// per unit for the combine kernel.
+__device__ bool plan_balanced(const DecodeParams& p, int tid, int lane, int wave, double* tot_sh,
+                              int* cnt_sh, int* item_sh, DecodeItem& it) {
+  constexpr int K = kPlanPerThread;
+  const int n_units = p.n_seq * p.hkv;
+  const int B = p.block_size;
+  const int u_first = tid * K;
+  // round trip 1: lengths and route bytes of this thread's units
+  int nraw[K], rbyte[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const int u = u_first + i;
+    nraw[i] = 1;
+    rbyte[i] = 0;
+    if (u < n_units) {
+      const int b = u / p.hkv, g = u - b * p.hkv;
+      nraw[i] = p.seqlens[b];
+      if (!p.compact) rbyte[i] = p.route[route_index(b, p.n_layers, p.layer, p.route_heads, g)];
+    }
+  }
+  // round trip 2: mask row bounds of the SA units
+  UnitKeys uk[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const int u = u_first + i;
+    uk[i].N = min(max(nraw[i], 1), p.max_len);
+    uk[i].fa = !p.compact && rbyte[i] != 0;
+    uk[i].mrow = min((uk[i].N - 1) / B, p.mask_blocks - 1);
+    uk[i].rp0 = 0;
+    uk[i].n_blk = 0;
+    if (u < n_units && !uk[i].fa) {
+      uk[i].rp0 = p.row_ptr[uk[i].mrow];
+      uk[i].n_blk = p.row_ptr[uk[i].mrow + 1];
+    }
+  }
+  double keys = 0.0;  // exact: fewer than 2^53 keys
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const int u = u_first + i;
+    uk[i].n_blk = min(max(uk[i].n_blk - uk[i].rp0, 0), uk[i].mrow + 1);
+    uk[i].U = u >= n_units ? 0 : uk[i].fa ? uk[i].N : uk[i].n_blk * B;
+    keys += static_cast<double>(uk[i].U);
+  }
+  // all keys of the call
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) keys += __shfl_xor(keys, o);
+  if (lane == 0) tot_sh[wave] = keys;
+  if (tid == 0) item_sh[0] = -1;
+  __syncthreads();
+  double total = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) total += tot_sh[w];
+  // items per unit when about `target` items share the keys: items of at
+  // most T = ceil(total / target) keys, i.e. s_u = ceil(U_u / T) (at least
+  // one, never below 256 keys each).  total / target is correctly rounded
+  // and a non-integer quotient lies at least 1 / target >= 2^-10 from every
+  // integer, while rounding moves it by at most 2^-12 (total < 2^41): the
+  // ceiling of the double quotient is the exact ceiling.
+  int sv[K];
+  auto shares = [&](int target) {
+    const double q = __builtin_ceil(total / static_cast<double>(target));
+    const uint32_t T = q < 2147483647.0 ? max(static_cast<uint32_t>(q), 1u) : 2147483647u;
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const int u = u_first + i;
+      const uint32_t U = static_cast<uint32_t>(uk[i].U);
+      const int by_size = static_cast<int>((U + T - 1) / T);
+      sv[i] = u >= n_units ? 0 : max(1, min(by_size, uk[i].U / kDecodeMinItemKeys));
+      mine += sv[i];
+    }
+    return mine;
+  };
+  // block-wide exclusive prefix of the item counts (threads in unit order);
+  // returns the thread's first slot, `all` gets the call's item count
+  auto prefix = [&](int mine, int* sh, int& all) {
+    int x = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) sh[wave] = x;
+    __syncthreads();
+    int first = x - mine;
+    all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = sh[w];
+      if (w < wave) first += c;
+      all += c;
+    }
+    return first;
+  };
+  // Rounding each unit up adds half an item per unit on average, so the first
+  // pass aims at 1024 - n_units / 2 items.  If the count passes the grid
+  // (min(1024, n_units + max keys / 256) workgroups), the second pass aims
+  // at 1024 - n_units: sum ceil(U_u / T) <= total / T + n_units <= 1024.
+  int all = 0;
+  int first = prefix(shares(kDecodeTargetItems - n_units / 2), cnt_sh, all);
+  if (all > p.slots) first = prefix(shares(max(kDecodeTargetItems - n_units, 1)), cnt_sh + kWaves, all);
+  const int item = blockIdx.x;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const int u = u_first + i;
+    if (u < n_units) {
+      if (item >= first && item < first + sv[i]) {
+        const int b = u / p.hkv;
+        item_sh[0] = b;
+        item_sh[1] = u - b * p.hkv;
+        item_sh[2] = item - first;
+        item_sh[3] = sv[i];
+        item_sh[4] = uk[i].N;
+        item_sh[5] = uk[i].fa;
+        item_sh[6] = uk[i].mrow;
+        item_sh[7] = uk[i].rp0;
+        item_sh[8] = uk[i].n_blk;
+        item_sh[9] = uk[i].U;
+      }
+      if (blockIdx.x == 0 && p.plan != nullptr) p.plan[u] = int2{first, sv[i]};
+    }
+    first += sv[i];
+  }
+  __syncthreads();
+  it.b = __builtin_amdgcn_readfirstlane(item_sh[0]);
+  if (it.b < 0) return false;
+  it.g = __builtin_amdgcn_readfirstlane(item_sh[1]);
+  it.j = __builtin_amdgcn_readfirstlane(item_sh[2]);
+  it.s = __builtin_amdgcn_readfirstlane(item_sh[3]);
+  it.N = __builtin_amdgcn_readfirstlane(item_sh[4]);
+  it.fa = __builtin_amdgcn_readfirstlane(item_sh[5]);
+  it.mrow = __builtin_amdgcn_readfirstlane(item_sh[6]);
+  it.rp0 = __builtin_amdgcn_readfirstlane(item_sh[7]);
+  it.n_blk = __builtin_amdgcn_readfirstlane(item_sh[8]);
+  const int U = __builtin_amdgcn_readfirstlane(item_sh[9]);
+  // contiguous, chunk-aligned range of the unit's visited keys
+  const int per = ((U + it.s - 1) / it.s + kChunk - 1) / kChunk * kChunk;
+  it.u0 = it.j * per;
+  it.u1 = min(U, it.u0 + per);
+  return true;
+}
+
+// One item per unit (calls with more units than the plan holds): the unit's
+// length and route byte in one gathered load, then, for SA, its mask row.
+__device__ __forceinline__ void plan_one_per_unit(const DecodeParams& p, int lane, DecodeItem& it) {
+  const int unit = blockIdx.x;
+  it.b = unit / p.hkv;
+  it.g = unit - it.b * p.hkv;
+  int gv = 0;
+  if (lane == 0)
+    gv = p.seqlens[it.b];
+  else if (lane == 1 && !p.compact)
+    gv = p.route[route_index(it.b, p.n_layers, p.layer, p.route_heads, it.g)];
+  const int n_raw = __builtin_amdgcn_readlane(gv, 0);
+  it.fa = !p.compact && __builtin_amdgcn_readlane(gv, 1) != 0;
+  it.N = min(max(n_raw, 1), p.max_len);
+  it.mrow = min((it.N - 1) / p.block_size, p.mask_blocks - 1);
+  it.rp0 = 0;
+  it.n_blk = 0;
+  if (!it.fa) {
+    it.rp0 = p.row_ptr[it.mrow];
+    it.n_blk = min(max(p.row_ptr[it.mrow + 1] - it.rp0, 0), it.mrow + 1);
+  }
+  it.j = 0;
+  it.s = 1;
+  it.u0 = 0;
+  it.u1 = it.fa ? it.N : it.n_blk * p.block_size;
+}
+
 template <int D>
 __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const DecodeParams p) {
   constexpr int KSTEPS = D / 32;      // k-steps of K Q^T
@@ -56,42 +253,32 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   constexpr int MERGE_BYTES = kWaves * (16 * D + 32) * 4;
   constexpr int LDS_BYTES = kWaves * VT_BYTES > MERGE_BYTES ? kWaves * VT_BYTES : MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+  __shared__ double plan_keys[kWaves];  // the plan's per-wave key sums
+  __shared__ int plan_cnt[2 * kWaves];  // ... and item counts (two passes at most)
+  __shared__ int plan_item[10];         // the item this workgroup takes
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, quarter = lane >> 4;
-
-  const int split = blockIdx.x % p.nsplit;
-  const int unit = blockIdx.x / p.nsplit;
-  const int b = unit / p.hkv, g = unit % p.hkv;
   const int group = p.hq / p.hkv;
 
-  // The sequence length and the route byte do not depend on each other and
-  // are read together; only an SA layer then reads its mask row (bounds, then
-  // the first 64 columns, lane i keeping column i), so an FA layer's first
-  // K/V loads wait on one round trip and an SA layer's on three.
-  // (one gathered load: lane 0 the length, lane 1 the route byte; a compact
-  // cache only holds an SA layer's rows and comes without a route)
-  int gv = 0;
-  if (lane == 0)
-    gv = p.seqlens[b];
-  else if (lane == 1 && !p.compact)
-    gv = p.route[route_index(b, p.n_layers, p.layer, p.route_heads, g)];
-  const int n_raw = __builtin_amdgcn_readlane(gv, 0);
-  const bool fa = !p.compact && __builtin_amdgcn_readlane(gv, 1) != 0;
-  const int N = min(max(n_raw, 1), p.max_len);
-  const int B = p.block_size;
-  const int mrow = min((N - 1) / B, p.mask_blocks - 1);
-  int rp0 = 0, n_blk = 0, col_lane = 0;
-  if (!fa) {
-    rp0 = p.row_ptr[mrow];
-    n_blk = max(p.row_ptr[mrow + 1] - rp0, 0);
-    col_lane = lane < n_blk ? min(max(p.col_idx[rp0 + lane], 0), mrow) : 0;
+  // The plan reads every unit's length and route byte in one round trip and
+  // the SA units' mask-row bounds in a second; the item's SA columns (first
+  // 64, lane i keeping column i) come in a third.  An FA item's first K/V
+  // loads therefore wait on two round trips and an SA item's on three.
+  DecodeItem it;
+  if (p.balanced) {
+    if (!plan_balanced(p, tid, lane, wave, plan_keys, plan_cnt, plan_item, it)) return;
+  } else {
+    plan_one_per_unit(p, lane, it);
   }
-  const int U = fa ? N : n_blk * B;
-  // contiguous range of visited-key indices for this split, chunk aligned
-  const int per = ((U + p.nsplit - 1) / p.nsplit + kChunk - 1) / kChunk * kChunk;
-  const int u0 = split * per;
-  const int u1 = min(U, u0 + per);
+  const int b = it.b, g = it.g;
+  const bool fa = it.fa != 0;
+  const int N = it.N;
+  const int B = p.block_size;
+  const int mrow = it.mrow;
+  const int rp0 = it.rp0, n_blk = it.n_blk;
+  const int col_lane = (!fa && lane < n_blk) ? min(max(p.col_idx[rp0 + lane], 0), mrow) : 0;
+  const int u0 = it.u0, u1 = it.u1;
 
   const size_t cache_head = static_cast<size_t>(p.cache_rows) * D;
   const uint16_t* kc = p.k_cache + (static_cast<size_t>(b) * p.hkv + g) * cache_head;
@@ -299,12 +486,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
       l += sc * ml[w * 16 + n];
     }
     const int head = g * group + n;
-    const size_t slot = (static_cast<size_t>(b) * p.hq + head) * p.nsplit + split;
-    if (p.nsplit == 1) {
+    if (it.s == 1) {  // the unit's only item: the result itself
       const float val = l > 0.0f ? o / l : 0.0f;
       const uint32_t bits = pack_bf16x2(val, 0.0f);
       p.out[(static_cast<size_t>(b) * p.hq + head) * D + dd] = static_cast<uint16_t>(bits & 0xffffu);
-    } else {
+    } else {  // partial of slot blockIdx.x, query column n
+      const size_t slot = static_cast<size_t>(blockIdx.x) * group + n;
       p.part_o[slot * D + dd] = o;
       if (dd == 0) {
         p.part_ml[slot * 2] = m;
@@ -314,46 +501,47 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   }
 }
 
-// Merge the nsplit partials of one (sequence, head): one thread per d.  Up
-// to kCombineBatch splits are read with all their loads in flight together
-// (one memory round trip); the sum runs over the splits in order either way.
+// Merge the items' partials of one (sequence, head): one thread per d.  The
+// unit's items occupy consecutive slots (first slot and count from the
+// plan); kCombineBatch partials at a time are read with all their loads in
+// flight together, and the batches are folded into the running result in
+// slot order, so the sum runs over the items in order.
 constexpr int kCombineBatch = 16;
 
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p) {
   const int sh = blockIdx.x;  // b * hq + head
   const int dd = threadIdx.x;
-  const int ns = p.nsplit;
-  const float* ml = p.part_ml + static_cast<size_t>(sh) * ns * 2;
-  const float* po = p.part_o + static_cast<size_t>(sh) * ns * D;
+  const int group = p.hq / p.hkv;
+  const int b = sh / p.hq, head = sh - b * p.hq;
+  const int u = b * p.hkv + head / group, n = head % group;
+  const int2 pl = p.plan[u];
+  const int first = pl.x, ns = pl.y;
+  if (ns <= 1) return;  // the split kernel wrote the result itself
   float m = kNegInf, o = 0.0f, l = 0.0f;
-  if (ns <= kCombineBatch) {
+  for (int s0 = 0; s0 < ns; s0 += kCombineBatch) {
     float mv[kCombineBatch], lv[kCombineBatch], ov[kCombineBatch];
 #pragma unroll
     for (int s = 0; s < kCombineBatch; ++s) {
-      const bool ok = s < ns;
-      mv[s] = ok ? ml[s * 2] : kNegInf;
-      lv[s] = ok ? ml[s * 2 + 1] : 0.0f;
-      ov[s] = ok ? po[static_cast<size_t>(s) * D + dd] : 0.0f;
+      const bool ok = s0 + s < ns;
+      const size_t slot = static_cast<size_t>(first + s0 + s) * group + n;
+      mv[s] = ok ? p.part_ml[slot * 2] : kNegInf;
+      lv[s] = ok ? p.part_ml[slot * 2 + 1] : 0.0f;
+      ov[s] = ok ? p.part_o[slot * D + dd] : 0.0f;
     }
+    float mb = m;
 #pragma unroll
-    for (int s = 0; s < kCombineBatch; ++s) m = fmaxf(m, mv[s]);
+    for (int s = 0; s < kCombineBatch; ++s) mb = fmaxf(mb, mv[s]);
+    const float sc0 = (m == kNegInf) ? 0.0f : fast_exp2(m - mb);
+    o *= sc0;
+    l *= sc0;
 #pragma unroll
     for (int s = 0; s < kCombineBatch; ++s) {
-      if (s < ns) {
-        const float sc = (mv[s] == kNegInf) ? 0.0f : fast_exp2(mv[s] - m);
-        o += sc * ov[s];
-        l += sc * lv[s];
-      }
+      const float sc = (mv[s] == kNegInf) ? 0.0f : fast_exp2(mv[s] - mb);
+      o += sc * ov[s];
+      l += sc * lv[s];
     }
-  } else {
-    for (int s = 0; s < ns; ++s) m = fmaxf(m, ml[s * 2]);
-    for (int s = 0; s < ns; ++s) {
-      const float ms = ml[s * 2];
-      const float sc = (ms == kNegInf) ? 0.0f : fast_exp2(ms - m);
-      o += sc * po[static_cast<size_t>(s) * D + dd];
-      l += sc * ml[s * 2 + 1];
-    }
+    m = mb;
   }
   const float val = l > 0.0f ? o / l : 0.0f;
   p.out[static_cast<size_t>(sh) * D + dd] = static_cast<uint16_t>(pack_bf16x2(val, 0.0f) & 0xffffu);
@@ -361,25 +549,41 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p)
 
 template <int D>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t s) {
-  const int64_t grid = static_cast<int64_t>(p.n_seq) * p.hkv * p.nsplit;
-  decode_split_kernel<D><<<dim3(static_cast<uint32_t>(grid)), dim3(kWaves * 64), 0, s>>>(p);
+  decode_split_kernel<D><<<dim3(static_cast<uint32_t>(p.slots)), dim3(kWaves * 64), 0, s>>>(p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.nsplit == 1) return e;
+  if (e != hipSuccess || p.slots <= p.n_seq * p.hkv) return e;  // one item per unit: no partials
   decode_combine_kernel<D><<<dim3(static_cast<uint32_t>(p.n_seq * p.hq)), dim3(D), 0, s>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int32_t decode_splits(int32_t n_seq, int32_t hkv, int32_t max_len) {
-  // Aim at ~1024 workgroups (4 per CU over 256 CUs) but keep >= 256 keys per split.
+DecodeShape decode_shape(int32_t n_seq, int32_t hkv, int32_t max_len) {
+  DecodeShape sh{};
   const int64_t units = static_cast<int64_t>(n_seq) * hkv;
-  int64_t s = (1024 + units - 1) / units;
-  const int64_t cap = (static_cast<int64_t>(max_len) + 255) / 256;
-  if (s > cap) s = cap;
-  if (s < 1) s = 1;
-  if (s > 64) s = 64;
-  return static_cast<int32_t>(s);
+  if (units > kDecodePlanUnits) {  // one item per unit
+    sh.balanced = 0;
+    sh.slots = units;
+    return sh;
+  }
+  // A unit visits at most max_len keys (FA) or ceil(max_len / B) whole blocks
+  // (SA), i.e. fewer than max_len + 128, and gets at most
+  // max(1, min(U * 1024 / total, U / 256)) items: in all at most n_units +
+  // min(1024, total / 256).
+  // The plan keeps the count within the grid: at most 1024 workgroups.
+  const int64_t most = units * (static_cast<int64_t>(max_len) + 127) / kDecodeMinItemKeys;
+  sh.balanced = 1;
+  sh.slots = units + most < kDecodeTargetItems ? units + most : kDecodeTargetItems;
+  return sh;
+}
+
+size_t decode_workspace_bytes(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_dim,
+                              int32_t max_len) {
+  const DecodeShape sh = decode_shape(n_seq, hkv, max_len);
+  const size_t units = static_cast<size_t>(n_seq) * hkv;
+  if (static_cast<size_t>(sh.slots) <= units) return 0;  // one item per unit: no partials
+  const size_t partials = static_cast<size_t>(sh.slots) * (hq / hkv) * (head_dim + 2) * sizeof(float);
+  return partials + units * sizeof(int2);
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {

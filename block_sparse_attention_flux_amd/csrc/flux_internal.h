@@ -32,10 +32,13 @@ struct DecodeParams {
   const uint8_t* route;
   const int32_t* row_ptr;
   const int32_t* col_idx;
-  float* part_o;   // [n_seq][hq][nsplit][head_dim]
-  float* part_ml;  // [n_seq][hq][nsplit][2]
+  float* part_o;   // [slots][hq / hkv][head_dim]  (partial of item slot, query column)
+  float* part_ml;  // [slots][hq / hkv][2]         (its running max and sum)
+  int2* plan;      // [n_seq * hkv]: (first slot, items) of each (sequence, kv head)
   int32_t n_seq, max_len, hq, hkv, head_dim, n_layers, layer, mask_blocks;
-  int32_t block_size, nsplit;
+  int32_t block_size;
+  int32_t slots;     // workgroups launched (work-item slots)
+  int32_t balanced;  // 1: items sized by keys (decode_shape); 0: one item per unit
   int32_t route_heads;                // route decisions per (sequence, layer): 1 or hkv
   int32_t cache_rows;                 // rows per (sequence, kv head) in the caches
   int32_t compact;                    // 1: SA cache of sink rows + a ring of window rows
@@ -100,8 +103,21 @@ hipError_t launch_route(const void* hidden, int32_t bf16, const int32_t* cu, int
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 
-// Number of KV splits the decode kernel uses for these sizes.
-int32_t decode_splits(int32_t n_seq, int32_t hkv, int32_t max_len);
+// Decode work items.  Each (sequence, kv head) unit visits U keys (FA: the
+// sequence's N keys; SA: its mask row's blocks); a call with at most
+// kDecodePlanUnits units cuts them into items of about total / 1024 keys
+// (at least kDecodeMinItemKeys), planned on the device by every workgroup;
+// larger calls take one item per unit.
+constexpr int32_t kDecodePlanUnits = 1024;
+constexpr int32_t kDecodeTargetItems = 1024;
+constexpr int32_t kDecodeMinItemKeys = 256;
+struct DecodeShape {
+  int64_t slots;     // workgroups to launch (an upper bound on the items)
+  int32_t balanced;  // 1: keys-balanced items; 0: one item per unit
+};
+DecodeShape decode_shape(int32_t n_seq, int32_t hkv, int32_t max_len);
+// Bytes of the decode workspace: partials of every slot, then the plan.
+size_t decode_workspace_bytes(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_dim,
+                              int32_t max_len);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
-
 }  // namespace flux

@@ -241,7 +241,15 @@ size_t flux_attn_decode_workspace_size(int32_t n_seq, int32_t hq, int32_t hkv,
                                        int32_t head_dim, int32_t max_len);
 
 /*
- * flux_attn_decode -- one decode step of one layer, split-KV.
+ * flux_attn_decode -- one decode step of one layer, split-KV over a work
+ * list: every (sequence, kv head) visits U keys (FA: its N keys; SA: its
+ * mask row's blocks), and the keys of all of them are cut into work items
+ * of about the same size (at most 1024 items per call, at least 256 keys
+ * each; a call with more than 1024 (sequence, kv head) pairs takes one item
+ * per pair), so a long FA sequence beside short SA sequences is split
+ * finer than they are.  The plan is made on the device from the lengths and
+ * routes of the call; the partial results of a pair's items are merged by
+ * the log-sum-exp rule.
  * The route fixed at prefill is reused for every decode step; SA layers read
  * only the keys of their mask row and never the rest of the history
  * (technical summary, section 2, deployment paragraph).
@@ -255,8 +263,11 @@ size_t flux_attn_decode_workspace_size(int32_t n_seq, int32_t hq, int32_t hkv,
  * seqlens     [device] int32 [n_seq], each in [1, max_len] (clamped on device)
  * route       [device] uint8 [n_seq][n_layers], read at [b][layer]; 1 = FA
  * mask_*      as for flux_attn_prefill, mask_blocks >= ceil(max_len / block_size)
- * workspace   [device] >= flux_attn_decode_workspace_size(...) bytes, any
- *             contents; it holds fp32 split partials between two kernels.
+ * workspace   [device] 16-byte aligned, >= flux_attn_decode_workspace_size(...)
+ *             bytes, any contents (nothing needs to start at zero); it holds
+ *             the items' fp32 partials and the work plan between two kernels.
+ *             When that size is 0 (every pair can only have one item: more
+ *             than 1024 pairs, or too few keys to split) it may be NULL.
  * Supported: head_dim in {64, 128}, block_size in {64, 128}, hq % hkv == 0,
  *            hq / hkv <= 16.
  */

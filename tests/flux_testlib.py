@@ -17,14 +17,13 @@ FROB_RTOL = 1e-2
 
 
 def ensure_built():
-    """Build libflux.so only when nothing is built yet."""
-    if os.path.exists(LIB):
-        return LIB
+    """Build libflux.so unless it is built from exactly the current sources
+    (the build's stamp: sha256 of sources, headers and flags)."""
     spec = importlib.util.spec_from_file_location(
         "flux_build", os.path.join(ROOT, "block_sparse_attention_flux_amd", "build.py"))
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
-    return mod.build()
+    return mod.ensure_built()
 
 
 def attn_errors(got, ref):

@@ -126,6 +126,25 @@ def test_prefill_validation(kw, code):
     assert prefill(**kw) == code
 
 
+def test_decode_workspace_size():
+    """Workspace = fp32 partials (head_dim values + max + sum) of every work-item
+    slot for each query head of a kv group, then one (first slot, count) pair
+    per (sequence, kv head).  Slots: at most 1024, and at most the pairs plus
+    one per 256 keys a call can visit; 0 when no pair can be split."""
+    def size(n, hq, hkv, d, ml):
+        return lib.flux_attn_decode_workspace_size(n, hq, hkv, d, ml)
+    units = 16 * 8
+    assert size(16, 32, 8, 128, 32768) == 1024 * 4 * (128 + 2) * 4 + units * 8
+    assert size(2, 4, 2, 64, 300) == (4 + 4 * 427 // 256) * 2 * 66 * 4 + 4 * 8
+    assert size(1, 1, 1, 64, 128) == 0          # 255 keys at most: never split
+    assert size(1, 1, 1, 64, 129) > 0
+    assert size(129, 32, 8, 128, 4096) == 0     # 1032 pairs: one item each
+    assert size(128, 32, 8, 128, 4096) == 0     # 1024 pairs fill the 1024 slots
+    assert size(127, 32, 8, 128, 4096) > 0
+    assert size(0, 32, 8, 128, 32768) == 0
+    assert size(16, 30, 8, 128, 32768) == 0     # hq not a multiple of hkv
+
+
 def test_decode_validation():
     ws = lib.flux_attn_decode_workspace_size(16, 32, 8, 128, 32768)
     assert ws > 0 and ws % 4 == 0
@@ -146,6 +165,7 @@ def test_decode_validation():
     assert dec(d=80) == -2
     assert dec(ws=NULL) == -3
     assert dec(wsb=ws - 4) == -3
+    assert dec(ws=ctypes.c_void_p(0x1008)) == -3   # not 16-byte aligned
 
 
 def test_binding_rejects_host_tensors():
