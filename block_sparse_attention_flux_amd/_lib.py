@@ -17,6 +17,7 @@ FLUX_ERR_WORKSPACE = -3
 FLUX_ERR_HIP = -4
 FLUX_F32 = 0
 FLUX_BF16 = 1
+FLUX_DECODE_SCRATCH_BYTES = 9 << 20
 
 
 class SAParamsC(ctypes.Structure):
@@ -53,6 +54,8 @@ SIGNATURES = [
                                      _P, _I, SAParamsC, _P]),
     ("flux_attn_prefill_soft", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P,
                                     _P, _I, SAParamsC, _P]),
+    ("flux_attn_decode_noalloc", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P, _P,
+                                      _I, SAParamsC, _P]),
     ("flux_attn_decode_heads", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P, _P,
                                     _I, SAParamsC, _P, _S, _P]),
     ("flux_kv_rows", ctypes.c_int64, [_I, SAParamsC, _I]),

@@ -78,13 +78,23 @@ flux_status attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
 
 // Work-item shape and workspace pointers of a decode call.  The workspace is
 // needed (and checked) only when a call can have more items than units.
+// With use_scratch the device's scratch array stands in for the workspace
+// (looked up only after every other check has passed).
 flux_status decode_layout(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_dim, int32_t max_len,
-                          void* workspace, size_t workspace_bytes, flux::DecodeParams* dp) {
+                          void* workspace, size_t workspace_bytes, bool use_scratch,
+                          void* stream, flux::DecodeParams* dp) {
   const flux::DecodeShape sh = flux::decode_shape(n_seq, hkv, max_len);
   if (sh.slots > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
   const int64_t units = static_cast<int64_t>(n_seq) * hkv;
   const bool partials = sh.slots > units;
   const size_t need = flux::decode_workspace_bytes(n_seq, hq, hkv, head_dim, max_len);
+  if (use_scratch) {
+    if (need > flux::kDecodeScratchBytes) return FLUX_ERR_WORKSPACE;
+    workspace_bytes = flux::kDecodeScratchBytes;
+    if (partials &&
+        flux::decode_scratch(static_cast<hipStream_t>(stream), &workspace) != hipSuccess)
+      return FLUX_ERR_HIP;
+  }
   if (partials && (workspace == nullptr || workspace_bytes < need ||
                    reinterpret_cast<uintptr_t>(workspace) % 16 != 0))
     return FLUX_ERR_WORKSPACE;
@@ -104,7 +114,8 @@ flux_status attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16
                         const uint8_t* route, int32_t n_layers, int32_t layer,
                         const int32_t* mask_row_ptr, const int32_t* mask_col_idx,
                         int32_t mask_blocks, flux_sa_params p, int32_t route_heads,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        bool use_scratch = false) {
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr ||
       seqlens == nullptr)
     return FLUX_ERR_INVALID_ARG;
@@ -115,7 +126,7 @@ flux_status attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16
   if (st != FLUX_OK) return st;
   flux::DecodeParams dp{};
   const flux_status ws = decode_layout(n_seq, hq, hkv, head_dim, max_len, workspace,
-                                       workspace_bytes, &dp);
+                                       workspace_bytes, use_scratch, stream, &dp);
   if (ws != FLUX_OK) return ws;
   dp.q = q; dp.k_cache = k_cache; dp.v_cache = v_cache; dp.out = out;
   dp.seqlens = seqlens; dp.route = route; dp.row_ptr = mask_row_ptr; dp.col_idx = mask_col_idx;
@@ -297,6 +308,21 @@ flux_status flux_attn_decode(const uint16_t* q, const uint16_t* k_cache, const u
                      mask_blocks, p, 1, workspace, workspace_bytes, stream);
 }
 
+flux_status flux_attn_decode_noalloc(const uint16_t* q, const uint16_t* k_cache,
+                                     const uint16_t* v_cache, uint16_t* out,
+                                     const int32_t* seqlens, int32_t n_seq, int32_t max_len,
+                                     int32_t hq, int32_t hkv, int32_t head_dim,
+                                     float softmax_scale, const uint8_t* route, int32_t n_layers,
+                                     int32_t layer, const int32_t* mask_row_ptr,
+                                     const int32_t* mask_col_idx, int32_t mask_blocks,
+                                     flux_sa_params p, void* stream) {
+  // the device's scratch array stands in for the workspace; a call that needs
+  // more than it holds returns FLUX_ERR_WORKSPACE
+  return attn_decode(q, k_cache, v_cache, out, seqlens, n_seq, max_len, hq, hkv, head_dim,
+                     softmax_scale, route, n_layers, layer, mask_row_ptr, mask_col_idx,
+                     mask_blocks, p, 1, nullptr, 0, stream, true);
+}
+
 flux_status flux_attn_decode_heads(const uint16_t* q, const uint16_t* k_cache,
                                    const uint16_t* v_cache, uint16_t* out, const int32_t* seqlens,
                                    int32_t n_seq, int32_t max_len, int32_t hq, int32_t hkv,
@@ -375,7 +401,7 @@ flux_status flux_attn_decode_sa_compact(const uint16_t* q, const uint16_t* k_cac
   if (sc != FLUX_OK) return sc;
   flux::DecodeParams dp{};
   const flux_status ws = decode_layout(n_seq, hq, hkv, head_dim, max_len, workspace,
-                                       workspace_bytes, &dp);
+                                       workspace_bytes, false, stream, &dp);
   if (ws != FLUX_OK) return ws;
   dp.q = q; dp.k_cache = k_cache; dp.v_cache = v_cache; dp.out = out;
   dp.seqlens = seqlens; dp.route = nullptr; dp.row_ptr = mask_row_ptr; dp.col_idx = mask_col_idx;

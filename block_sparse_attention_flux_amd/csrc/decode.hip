@@ -23,11 +23,20 @@
 //   the 4 waves of a workgroup merge their (max, sum, O) through LDS, and a
 //               second small kernel merges the splits with the log-sum-exp
 //               rule  O = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s.
+#include <mutex>
+
 #include "flux_device.h"
 #include "flux_internal.h"
 
 namespace flux {
 namespace {
+
+// Device-resident scratch of flux_attn_decode_noalloc: the same partials
+// and plan as a caller's workspace, for callers that cannot allocate.  One
+// copy per GPU, held until the process ends; its host-side name is not a
+// device address, so host code uses only the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
 
 constexpr int kWaves = 4;
 constexpr int kChunk = 32;                  // keys per wave iteration
@@ -584,6 +593,33 @@ size_t decode_workspace_bytes(int32_t n_seq, int32_t hq, int32_t hkv, int32_t he
   if (static_cast<size_t>(sh.slots) <= units) return 0;  // one item per unit: no partials
   const size_t partials = static_cast<size_t>(sh.slots) * (hq / hkv) * (head_dim + 2) * sizeof(float);
   return partials + units * sizeof(int2);
+}
+
+hipError_t decode_scratch(hipStream_t stream, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {

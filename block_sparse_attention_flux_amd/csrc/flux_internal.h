@@ -120,4 +120,14 @@ DecodeShape decode_shape(int32_t n_seq, int32_t hkv, int32_t max_len);
 size_t decode_workspace_bytes(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_dim,
                               int32_t max_len);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+// The decode scratch array of the device that `stream` belongs to (looked up
+// once per device with hipGetSymbolAddress; allocates nothing).
+constexpr size_t kDecodeScratchBytes = size_t(9) << 20;  // FLUX_DECODE_SCRATCH_BYTES
+// The largest workspace a valid call needs: 1024 slots x 16 query heads per
+// kv head x (128 + 2) floats, plus the plan of 1024 units.
+static_assert(size_t(kDecodeTargetItems) * 16 * (128 + 2) * 4 + size_t(kDecodePlanUnits) * 8 <=
+                  kDecodeScratchBytes,
+              "the decode scratch must hold the largest workspace");
+hipError_t decode_scratch(hipStream_t stream, void** ptr);
+
 }  // namespace flux

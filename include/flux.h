@@ -13,8 +13,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Pointers marked [device] are HIP device pointers; [host] are host memory.
- *   The caller allocates and frees every buffer.  The library keeps no mutable
- *   global state and never allocates on these paths.
+ *   The caller allocates and frees every buffer.  The library never
+ *   allocates on these paths and keeps no mutable global state, except the
+ *   device scratch array of flux_attn_decode_noalloc (one per GPU).
  * - bf16 tensors are passed as raw bf16 bit patterns (uint16_t).
  * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *   Every call is asynchronous on `stream` and never synchronises it.
@@ -279,6 +280,32 @@ flux_status flux_attn_decode(const uint16_t* q, const uint16_t* k_cache,
                              const int32_t* mask_col_idx, int32_t mask_blocks,
                              flux_sa_params p, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * flux_attn_decode_noalloc -- flux_attn_decode without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * split partials and the work plan live in a device array of the library
+ * (FLUX_DECODE_SCRATCH_BYTES, one copy per GPU, kept until the process ends;
+ * its address is looked up once per device).  Nothing is allocated and
+ * nothing needs to start at zero.  Calls on one GPU share that array: calls
+ * that may overlap in time on one GPU (different streams, or host threads)
+ * race and give wrong results; calls ordered on one stream are safe.
+ * The array holds FLUX_DECODE_SCRATCH_BYTES (9 MiB); the largest workspace
+ * any call that flux_attn_decode accepts can need is 8.2 MiB (1024 work
+ * items x 16 query heads per kv head x head_dim 128), and a call needing
+ * more than the array would return FLUX_ERR_WORKSPACE.  Everything else,
+ * including the results (bit for bit), as flux_attn_decode.
+ */
+#define FLUX_DECODE_SCRATCH_BYTES ((size_t)9 << 20)
+flux_status flux_attn_decode_noalloc(const uint16_t* q, const uint16_t* k_cache,
+                                     const uint16_t* v_cache, uint16_t* out,
+                                     const int32_t* seqlens, int32_t n_seq, int32_t max_len,
+                                     int32_t hq, int32_t hkv, int32_t head_dim,
+                                     float softmax_scale, const uint8_t* route, int32_t n_layers,
+                                     int32_t layer, const int32_t* mask_row_ptr,
+                                     const int32_t* mask_col_idx, int32_t mask_blocks,
+                                     flux_sa_params p, void* stream);
 
 /* flux_attn_decode_heads -- flux_attn_decode with route uint8
  * [n_seq][n_layers][hkv], one decision per kv head (see flux_attn_prefill_heads). */

@@ -31,7 +31,7 @@ def declared_symbols(header=HEADER):
 
 def test_exports_every_declared_symbol():
     syms = declared_symbols()
-    assert len(syms) == 18, syms
+    assert len(syms) == 19, syms
     raw = ctypes.CDLL(LIB)
     for s in syms:
         assert hasattr(raw, s), s
@@ -143,6 +143,33 @@ def test_decode_workspace_size():
     assert size(127, 32, 8, 128, 4096) > 0
     assert size(0, 32, 8, 128, 32768) == 0
     assert size(16, 30, 8, 128, 32768) == 0     # hq not a multiple of hkv
+
+
+def test_decode_noalloc_validation():
+    """flux_attn_decode_noalloc checks its arguments like flux_attn_decode
+    before any HIP call (so these run without a GPU); its device scratch holds
+    the largest workspace a valid call can need."""
+    assert _lib.FLUX_DECODE_SCRATCH_BYTES == 9 << 20
+    worst = max(lib.flux_attn_decode_workspace_size(n, 16 * hkv, hkv, 128, 1 << 20)
+                for n, hkv in ((1, 1), (16, 8), (127, 8), (64, 16), (1023, 1)))
+    assert 8 << 20 < worst <= _lib.FLUX_DECODE_SCRATCH_BYTES
+
+    def dec(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=ctypes.c_void_p(0x3000), sl=FAKE, n=16, ml=32768, hq=32,
+                 hkv=8, d=128, scale=0.088, route=FAKE, L=36, layer=0, rp=FAKE, ci=FAKE, mb=256,
+                 sa=SA(128, 1, 16), stream=NULL)
+        a.update(kw)
+        return lib.flux_attn_decode_noalloc(a["q"], a["k"], a["v"], a["out"], a["sl"], a["n"], a["ml"],
+                                            a["hq"], a["hkv"], a["d"], a["scale"], a["route"], a["L"],
+                                            a["layer"], a["rp"], a["ci"], a["mb"], a["sa"], a["stream"])
+    assert dec(q=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(out=FAKE) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(route=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(hq=30) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(mb=255) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(layer=36) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(d=80) == _lib.FLUX_ERR_UNSUPPORTED
+    assert dec(hq=64, hkv=2) == _lib.FLUX_ERR_UNSUPPORTED   # 32 query heads per kv head
 
 
 def test_decode_validation():
