@@ -26,7 +26,7 @@ __all__ = [
     "SAParams", "FluxError", "route", "route_workspace_size", "mask_blocks", "mask_nnz", "build_block_mask",
     "build_block_mask_dynamic",
     "attn_prefill", "attn_prefill_soft", "decode_workspace_size", "decode_workspace", "attn_decode",
-    "attn_decode_noalloc", "status_str",
+    "attn_decode_append", "attn_decode_noalloc", "status_str",
     "kv_rows", "kv_cache", "kv_store_prefill", "kv_append", "attn_decode_sa_compact",
     "probe_mfma", "probe_read",
 ]
@@ -255,6 +255,38 @@ def attn_decode(q, k_cache, v_cache, seqlens, route, layer, row_ptr, col_idx, sa
         row_ptr.numel() - 1, sa.c(), _ptr(workspace, None, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(code, "flux_attn_decode")
+    return out
+
+
+def attn_decode_append(q, k_new, v_new, k_cache, v_cache, seqlens, route, layer, row_ptr, col_idx, sa,
+                       workspace=None, out=None, softmax_scale=None):
+    """One decode step of one layer with the new K/V row appended in the same
+    launch (flux_attn_decode_append): k_new, v_new [n_seq][hkv][head_dim] go to
+    position seqlens[b] - 1 of the full caches, which the step reads."""
+    n_seq, hq, d = q.shape
+    _, hkv, max_len, _ = k_cache.shape
+    if k_cache.shape != (n_seq, hkv, max_len, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [n_seq][hkv][max_len][head_dim]")
+    if k_new.shape != (n_seq, hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [n_seq][hkv][head_dim]")
+    if route.dim() != 2:
+        raise ValueError("attn_decode_append: route must be [n_seq][n_layers]")
+    if out is None:
+        out = torch.empty_like(q)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = decode_workspace(n_seq, hq, hkv, d, max_len, q.device)
+    code = _LIB.flux_attn_decode_append(
+        _ptr(q, torch.bfloat16, "q"), _ptr(k_new, torch.bfloat16, "k_new"),
+        _ptr(v_new, torch.bfloat16, "v_new"), _ptr(k_cache, torch.bfloat16, "k_cache"),
+        _ptr(v_cache, torch.bfloat16, "v_cache"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(seqlens, torch.int32, "seqlens"), n_seq, max_len, hq, hkv, d, float(softmax_scale),
+        _ptr(route, torch.uint8, "route"), route.shape[1], int(layer),
+        _ptr(row_ptr, torch.int32, "row_ptr"), _ptr(col_idx, torch.int32, "col_idx"),
+        row_ptr.numel() - 1, sa.c(), _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(code, "flux_attn_decode_append")
     return out
 
 

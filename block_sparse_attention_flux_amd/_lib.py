@@ -54,6 +54,8 @@ SIGNATURES = [
                                      _P, _I, SAParamsC, _P]),
     ("flux_attn_prefill_soft", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P,
                                     _P, _I, SAParamsC, _P]),
+    ("flux_attn_decode_append", _I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I,
+                                     _P, _P, _I, SAParamsC, _P, _S, _P]),
     ("flux_attn_decode_noalloc", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P, _P,
                                       _I, SAParamsC, _P]),
     ("flux_attn_decode_heads", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P, _P,

@@ -77,16 +77,17 @@ flux_status attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
 }
 
 // Work-item shape and workspace pointers of a decode call.  The workspace is
-// needed (and checked) only when a call can have more items than units.
-// With use_scratch the device's scratch array stands in for the workspace
-// (looked up only after every other check has passed).
+// needed (and checked) only when a call can have more items than units; it
+// is sized for the largest item target, so it is checked before the device
+// is queried for its own.  With use_scratch the device's scratch array stands
+// in for the workspace (looked up only after every other check has passed).
 flux_status decode_layout(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_dim, int32_t max_len,
-                          void* workspace, size_t workspace_bytes, bool use_scratch,
+                          void* workspace, size_t workspace_bytes, bool use_scratch, bool append,
                           void* stream, flux::DecodeParams* dp) {
-  const flux::DecodeShape sh = flux::decode_shape(n_seq, hkv, max_len);
-  if (sh.slots > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
+  const flux::DecodeShape most = flux::decode_shape(n_seq, hkv, max_len, flux::kDecodeMaxItems);
+  if (most.slots > INT32_MAX) return FLUX_ERR_UNSUPPORTED;
   const int64_t units = static_cast<int64_t>(n_seq) * hkv;
-  const bool partials = sh.slots > units;
+  const bool partials = most.slots > units;
   const size_t need = flux::decode_workspace_bytes(n_seq, hq, hkv, head_dim, max_len);
   if (use_scratch) {
     if (need > flux::kDecodeScratchBytes) return FLUX_ERR_WORKSPACE;
@@ -98,13 +99,16 @@ flux_status decode_layout(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_d
   if (partials && (workspace == nullptr || workspace_bytes < need ||
                    reinterpret_cast<uintptr_t>(workspace) % 16 != 0))
     return FLUX_ERR_WORKSPACE;
-  const size_t n_part = static_cast<size_t>(sh.slots) * (hq / hkv);
+  const int32_t target = flux::decode_target(static_cast<hipStream_t>(stream), head_dim, append);
+  const flux::DecodeShape sh = flux::decode_shape(n_seq, hkv, max_len, target);
+  const size_t n_part = static_cast<size_t>(most.slots) * (hq / hkv);
   float* ws = partials ? static_cast<float*>(workspace) : nullptr;
   dp->part_o = ws;
   dp->part_ml = ws != nullptr ? ws + n_part * head_dim : nullptr;
   dp->plan = ws != nullptr ? reinterpret_cast<int2*>(ws + n_part * (head_dim + 2)) : nullptr;
   dp->slots = static_cast<int32_t>(sh.slots);
   dp->balanced = sh.balanced;
+  dp->target = target;
   return FLUX_OK;
 }
 
@@ -115,7 +119,9 @@ flux_status attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16
                         const int32_t* mask_row_ptr, const int32_t* mask_col_idx,
                         int32_t mask_blocks, flux_sa_params p, int32_t route_heads,
                         void* workspace, size_t workspace_bytes, void* stream,
-                        bool use_scratch = false) {
+                        bool use_scratch = false, const uint16_t* k_new = nullptr,
+                        const uint16_t* v_new = nullptr, uint16_t* k_write = nullptr,
+                        uint16_t* v_write = nullptr) {
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr ||
       seqlens == nullptr)
     return FLUX_ERR_INVALID_ARG;
@@ -126,7 +132,7 @@ flux_status attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16
   if (st != FLUX_OK) return st;
   flux::DecodeParams dp{};
   const flux_status ws = decode_layout(n_seq, hq, hkv, head_dim, max_len, workspace,
-                                       workspace_bytes, use_scratch, stream, &dp);
+                                       workspace_bytes, use_scratch, k_new != nullptr, stream, &dp);
   if (ws != FLUX_OK) return ws;
   dp.q = q; dp.k_cache = k_cache; dp.v_cache = v_cache; dp.out = out;
   dp.seqlens = seqlens; dp.route = route; dp.row_ptr = mask_row_ptr; dp.col_idx = mask_col_idx;
@@ -135,6 +141,7 @@ flux_status attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16
   dp.block_size = p.block_size; dp.scale = softmax_scale;
   dp.cache_rows = max_len; dp.compact = 0; dp.route_heads = route_heads;
   dp.sink_blocks = p.sink_blocks; dp.local_blocks = p.local_blocks;
+  dp.k_new = k_new; dp.v_new = v_new; dp.k_write = k_write; dp.v_write = v_write;
   return from_hip(flux::launch_decode(dp, static_cast<hipStream_t>(stream)));
 }
 
@@ -323,6 +330,25 @@ flux_status flux_attn_decode_noalloc(const uint16_t* q, const uint16_t* k_cache,
                      mask_blocks, p, 1, nullptr, 0, stream, true);
 }
 
+flux_status flux_attn_decode_append(const uint16_t* q, const uint16_t* k_new,
+                                    const uint16_t* v_new, uint16_t* k_cache, uint16_t* v_cache,
+                                    uint16_t* out, const int32_t* seqlens, int32_t n_seq,
+                                    int32_t max_len, int32_t hq, int32_t hkv, int32_t head_dim,
+                                    float softmax_scale, const uint8_t* route, int32_t n_layers,
+                                    int32_t layer, const int32_t* mask_row_ptr,
+                                    const int32_t* mask_col_idx, int32_t mask_blocks,
+                                    flux_sa_params p, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (k_new == nullptr || v_new == nullptr) return FLUX_ERR_INVALID_ARG;
+  if (k_new == k_cache || k_new == v_cache || v_new == k_cache || v_new == v_cache ||
+      out == k_cache || out == v_cache || k_cache == v_cache)
+    return FLUX_ERR_INVALID_ARG;
+  return attn_decode(q, k_cache, v_cache, out, seqlens, n_seq, max_len, hq, hkv, head_dim,
+                     softmax_scale, route, n_layers, layer, mask_row_ptr, mask_col_idx,
+                     mask_blocks, p, 1, workspace, workspace_bytes, stream, false, k_new, v_new,
+                     k_cache, v_cache);
+}
+
 flux_status flux_attn_decode_heads(const uint16_t* q, const uint16_t* k_cache,
                                    const uint16_t* v_cache, uint16_t* out, const int32_t* seqlens,
                                    int32_t n_seq, int32_t max_len, int32_t hq, int32_t hkv,
@@ -401,7 +427,7 @@ flux_status flux_attn_decode_sa_compact(const uint16_t* q, const uint16_t* k_cac
   if (sc != FLUX_OK) return sc;
   flux::DecodeParams dp{};
   const flux_status ws = decode_layout(n_seq, hq, hkv, head_dim, max_len, workspace,
-                                       workspace_bytes, false, stream, &dp);
+                                       workspace_bytes, false, false, stream, &dp);
   if (ws != FLUX_OK) return ws;
   dp.q = q; dp.k_cache = k_cache; dp.v_cache = v_cache; dp.out = out;
   dp.seqlens = seqlens; dp.route = nullptr; dp.row_ptr = mask_row_ptr; dp.col_idx = mask_col_idx;

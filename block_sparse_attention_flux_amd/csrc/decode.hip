@@ -25,6 +25,8 @@
 //               rule  O = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s.
 #include <mutex>
 
+#include <type_traits>
+
 #include "flux_device.h"
 #include "flux_internal.h"
 
@@ -40,8 +42,6 @@ static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
 
 constexpr int kWaves = 4;
 constexpr int kChunk = 32;                  // keys per wave iteration
-constexpr int kPlanPerThread = kDecodePlanUnits / (kWaves * 64);  // units per thread in the plan
-static_assert(kPlanPerThread * kWaves * 64 == kDecodePlanUnits, "plan units must fill the workgroup");
 constexpr float kRescaleSlack = 8.0f;       // log2 units the stale max may lag
 constexpr int kVtPitch = kChunk * 2 + 16;   // bytes per V^T row in LDS
 
@@ -65,6 +65,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // j of the unit's s items (all values wave-uniform).
 struct DecodeItem {
   int b, g, j, s, N, fa, mrow, rp0, n_blk, u0, u1;
+  int app;  // a new row is appended at N - 1 (seqlens[b] in [1, max_len])
 };
 
 // The unit's length, route and mask row, clamped into range: N in
@@ -72,6 +73,9 @@ struct DecodeItem {
 struct UnitKeys {
   int N, fa, mrow, rp0, n_blk, U;
 };
+
+constexpr int kPlanPerThread = kDecodePlanUnits / (kWaves * 64);  // units per thread in the plan
+static_assert(kPlanPerThread * kWaves * 64 == kDecodePlanUnits, "plan units must fill the workgroup");
 
 // Balanced plan, computed by every workgroup for the whole call.  Thread t
 // owns units [4t, 4t + 4) (unit u = b * hkv + g).  With `total` the keys of
@@ -181,8 +185,8 @@ __device__ bool plan_balanced(const DecodeParams& p, int tid, int lane, int wave
   // (min(1024, n_units + max keys / 256) workgroups), the second pass aims
   // at 1024 - n_units: sum ceil(U_u / T) <= total / T + n_units <= 1024.
   int all = 0;
-  int first = prefix(shares(kDecodeTargetItems - n_units / 2), cnt_sh, all);
-  if (all > p.slots) first = prefix(shares(max(kDecodeTargetItems - n_units, 1)), cnt_sh + kWaves, all);
+  int first = prefix(shares(max(p.target - n_units / 2, 1)), cnt_sh, all);
+  if (all > p.slots) first = prefix(shares(max(p.target - n_units, 1)), cnt_sh + kWaves, all);
   const int item = blockIdx.x;
 #pragma unroll
   for (int i = 0; i < K; ++i) {
@@ -200,6 +204,7 @@ __device__ bool plan_balanced(const DecodeParams& p, int tid, int lane, int wave
         item_sh[7] = uk[i].rp0;
         item_sh[8] = uk[i].n_blk;
         item_sh[9] = uk[i].U;
+        item_sh[10] = nraw[i] >= 1 && nraw[i] <= p.max_len;
       }
       if (blockIdx.x == 0 && p.plan != nullptr) p.plan[u] = int2{first, sv[i]};
     }
@@ -217,6 +222,7 @@ __device__ bool plan_balanced(const DecodeParams& p, int tid, int lane, int wave
   it.rp0 = __builtin_amdgcn_readfirstlane(item_sh[7]);
   it.n_blk = __builtin_amdgcn_readfirstlane(item_sh[8]);
   const int U = __builtin_amdgcn_readfirstlane(item_sh[9]);
+  it.app = p.k_new != nullptr && __builtin_amdgcn_readfirstlane(item_sh[10]) != 0;
   // contiguous, chunk-aligned range of the unit's visited keys
   const int per = ((U + it.s - 1) / it.s + kChunk - 1) / kChunk * kChunk;
   it.u0 = it.j * per;
@@ -238,6 +244,7 @@ __device__ __forceinline__ void plan_one_per_unit(const DecodeParams& p, int lan
   const int n_raw = __builtin_amdgcn_readlane(gv, 0);
   it.fa = !p.compact && __builtin_amdgcn_readlane(gv, 1) != 0;
   it.N = min(max(n_raw, 1), p.max_len);
+  it.app = p.k_new != nullptr && n_raw >= 1 && n_raw <= p.max_len;
   it.mrow = min((it.N - 1) / p.block_size, p.mask_blocks - 1);
   it.rp0 = 0;
   it.n_blk = 0;
@@ -251,7 +258,9 @@ __device__ __forceinline__ void plan_one_per_unit(const DecodeParams& p, int lan
   it.u1 = it.fa ? it.N : it.n_blk * p.block_size;
 }
 
-template <int D>
+// APPEND: the step also appends the new K/V row (DecodeParams::k_new); a
+// separate instantiation, so the plain decode carries none of its code.
+template <int D, bool APPEND>
 __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const DecodeParams p) {
   constexpr int KSTEPS = D / 32;      // k-steps of K Q^T
   constexpr int DT = D / 16;          // 16-row tiles of O^T
@@ -262,18 +271,19 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   constexpr int MERGE_BYTES = kWaves * (16 * D + 32) * 4;
   constexpr int LDS_BYTES = kWaves * VT_BYTES > MERGE_BYTES ? kWaves * VT_BYTES : MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-  __shared__ double plan_keys[kWaves];  // the plan's per-wave key sums
-  __shared__ int plan_cnt[2 * kWaves];  // ... and item counts (two passes at most)
-  __shared__ int plan_item[10];         // the item this workgroup takes
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, quarter = lane >> 4;
   const int group = p.hq / p.hkv;
+  __shared__ double plan_keys[kWaves];  // the plan's per-wave key sums
+  __shared__ int plan_cnt[2 * kWaves];  // ... and item counts (two passes at most)
+  __shared__ int plan_item[11];         // the item this workgroup takes
 
   // The plan reads every unit's length and route byte in one round trip and
   // the SA units' mask-row bounds in a second; the item's SA columns (first
-  // 64, lane i keeping column i) come in a third.  An FA item's first K/V
-  // loads therefore wait on two round trips and an SA item's on three.
+  // 64, lane i keeping column i) come in a third.  An item's first K/V loads
+  // therefore wait on two or three round trips.  (A plan made by every wave
+  // on its own, with no LDS or barrier, measured slower: 4 us per SA layer.)
   DecodeItem it;
   if (p.balanced) {
     if (!plan_balanced(p, tid, lane, wave, plan_keys, plan_cnt, plan_item, it)) return;
@@ -292,6 +302,24 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   const size_t cache_head = static_cast<size_t>(p.cache_rows) * D;
   const uint16_t* kc = p.k_cache + (static_cast<size_t>(b) * p.hkv + g) * cache_head;
   const uint16_t* vc = p.v_cache + (static_cast<size_t>(b) * p.hkv + g) * cache_head;
+
+  // Fused append: the unit's last item writes the new row into the caches;
+  // whichever item visits key N - 1 reads it from k_new / v_new instead, so no
+  // item reads that row from the caches and no workgroup waits for another.
+  const int newk = APPEND && it.app ? N - 1 : -1;
+  const uint16_t* kn_row = nullptr;
+  const uint16_t* vn_row = nullptr;
+  if (APPEND && it.app) {
+    const size_t nrow = (static_cast<size_t>(b) * p.hkv + g) * D;
+    kn_row = p.k_new + nrow;
+    vn_row = p.v_new + nrow;
+    if (it.j == it.s - 1 && wave == 0 && lane < 2 * CH) {
+      const bool isv = lane >= CH;
+      const int c = isv ? lane - CH : lane;
+      const size_t dst = (static_cast<size_t>(b) * p.hkv + g) * cache_head + static_cast<size_t>(N - 1) * D + c * 8;
+      st16((isv ? p.v_write : p.k_write) + dst, ld16((isv ? vn_row : kn_row) + c * 8));
+    }
+  }
 
   // first key position of the chunk that starts at visited index u (wave-uniform)
   auto chunk_key = [&](int u) -> int {
@@ -343,25 +371,40 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
     k0 = chunk_key(u);
     limit = min(k0 + min(u1 - u, kChunk), N);
     const int row0 = cache_row(k0) - k0;  // row of key k is row0 + k within this chunk
+    // Rows come from the caches, except the appended key's, which comes from
+    // k_new / v_new (APPEND only: a per-lane choice of the row address; a
+    // wave-uniform branch to a second copy of the loads for the one chunk
+    // holding that key measured slower, it spilled registers).
+    auto rows = [&](auto with_new) {
+      constexpr bool kNew = decltype(with_new)::value;
+      auto krow = [&](int key) {
+        return kNew && key == newk ? kn_row : kc + static_cast<size_t>(row0 + key) * D;
+      };
+      auto vrow = [&](int key) {
+        return kNew && key == newk ? vn_row : vc + static_cast<size_t>(row0 + key) * D;
+      };
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int key = k0 + mt * 16 + l16;
+      for (int mt = 0; mt < 2; ++mt) {
+        const int key = k0 + mt * 16 + l16;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
-        kr[mt][ks] = key < limit ? ld16_stream(kc + static_cast<size_t>(row0 + key) * D + ks * 32 + quarter * 8)
-                                 : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < VQC; ++j) {
-      const int id = lane + 64 * j;
-      const int c = id % CH, qd = id / CH;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int key = k0 + qd * 4 + kk;
-        vr[j][kk] = key < limit ? ld16_stream(vc + static_cast<size_t>(row0 + key) * D + c * 8)
-                                : u32x4{0, 0, 0, 0};
+        for (int ks = 0; ks < KSTEPS; ++ks)
+          kr[mt][ks] = key < limit ? ld16_stream(krow(key) + ks * 32 + quarter * 8) : u32x4{0, 0, 0, 0};
       }
-    }
+#pragma unroll
+      for (int j = 0; j < VQC; ++j) {
+        const int id = lane + 64 * j;
+        const int c = id % CH, qd = id / CH;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int key = k0 + qd * 4 + kk;
+          vr[j][kk] = key < limit ? ld16_stream(vrow(key) + c * 8) : u32x4{0, 0, 0, 0};
+        }
+      }
+    };
+    if constexpr (APPEND)
+      rows(std::true_type{});
+    else
+      rows(std::false_type{});
   };
 
   auto compute_chunk = [&](const KRegs& kr, const VRegs& vr, int k0, int limit) {
@@ -510,64 +553,109 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   }
 }
 
-// Merge the items' partials of one (sequence, head): one thread per d.  The
-// unit's items occupy consecutive slots (first slot and count from the
-// plan); kCombineBatch partials at a time are read with all their loads in
-// flight together, and the batches are folded into the running result in
-// slot order, so the sum runs over the items in order.
+// Merge the items' partials of one (sequence, head).  The unit's items
+// occupy consecutive slots (first slot and count from the plan); lane l
+// holds d = l + 64 k.  Up to kCombineBatch items: wave 0 alone reads them
+// all with their loads in flight together and writes the result.  More:
+// wave w merges items w, w + 4, w + 8, ... (kCombineBatch at a time, all
+// loads in flight), then the 4 waves' results are merged through LDS in wave
+// order.  Either way the sum has a fixed order, and up to 64 items cost one
+// memory round trip.
 constexpr int kCombineBatch = 16;
+constexpr int kCombineWaves = 4;
 
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kCombineWaves * 64) void decode_combine_kernel(const DecodeParams p) {
+  constexpr int DPL = D / 64;  // d values per lane
+  __shared__ float wm[kCombineWaves], wl[kCombineWaves], wo[kCombineWaves][D];
   const int sh = blockIdx.x;  // b * hq + head
-  const int dd = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int group = p.hq / p.hkv;
   const int b = sh / p.hq, head = sh - b * p.hq;
   const int u = b * p.hkv + head / group, n = head % group;
   const int2 pl = p.plan[u];
   const int first = pl.x, ns = pl.y;
   if (ns <= 1) return;  // the split kernel wrote the result itself
-  float m = kNegInf, o = 0.0f, l = 0.0f;
-  for (int s0 = 0; s0 < ns; s0 += kCombineBatch) {
-    float mv[kCombineBatch], lv[kCombineBatch], ov[kCombineBatch];
+  const bool one_wave = ns <= kCombineBatch;
+  if (one_wave && wave != 0) return;
+  const int stride = one_wave ? 1 : kCombineWaves;
+  float m = kNegInf, l = 0.0f, o[DPL];
 #pragma unroll
-    for (int s = 0; s < kCombineBatch; ++s) {
-      const bool ok = s0 + s < ns;
-      const size_t slot = static_cast<size_t>(first + s0 + s) * group + n;
-      mv[s] = ok ? p.part_ml[slot * 2] : kNegInf;
-      lv[s] = ok ? p.part_ml[slot * 2 + 1] : 0.0f;
-      ov[s] = ok ? p.part_o[slot * D + dd] : 0.0f;
+  for (int k = 0; k < DPL; ++k) o[k] = 0.0f;
+  for (int s0 = one_wave ? 0 : wave; s0 < ns; s0 += stride * kCombineBatch) {
+    float mv[kCombineBatch], lv[kCombineBatch], ov[kCombineBatch][DPL];
+#pragma unroll
+    for (int t = 0; t < kCombineBatch; ++t) {
+      const int si = s0 + stride * t;
+      const bool ok = si < ns;
+      const size_t slot = static_cast<size_t>(first + (ok ? si : 0)) * group + n;
+      mv[t] = ok ? p.part_ml[slot * 2] : kNegInf;
+      lv[t] = ok ? p.part_ml[slot * 2 + 1] : 0.0f;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) ov[t][k] = ok ? p.part_o[slot * D + lane + 64 * k] : 0.0f;
     }
     float mb = m;
 #pragma unroll
-    for (int s = 0; s < kCombineBatch; ++s) mb = fmaxf(mb, mv[s]);
+    for (int t = 0; t < kCombineBatch; ++t) mb = fmaxf(mb, mv[t]);
     const float sc0 = (m == kNegInf) ? 0.0f : fast_exp2(m - mb);
-    o *= sc0;
     l *= sc0;
 #pragma unroll
-    for (int s = 0; s < kCombineBatch; ++s) {
-      const float sc = (mv[s] == kNegInf) ? 0.0f : fast_exp2(mv[s] - mb);
-      o += sc * ov[s];
-      l += sc * lv[s];
+    for (int k = 0; k < DPL; ++k) o[k] *= sc0;
+#pragma unroll
+    for (int t = 0; t < kCombineBatch; ++t) {
+      const float sc = (mv[t] == kNegInf) ? 0.0f : fast_exp2(mv[t] - mb);
+      l += sc * lv[t];
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) o[k] += sc * ov[t][k];
     }
     m = mb;
   }
-  const float val = l > 0.0f ? o / l : 0.0f;
-  p.out[static_cast<size_t>(sh) * D + dd] = static_cast<uint16_t>(pack_bf16x2(val, 0.0f) & 0xffffu);
+  uint16_t* dst = p.out + static_cast<size_t>(sh) * D;
+  if (one_wave) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+      dst[lane + 64 * k] = static_cast<uint16_t>(pack_bf16x2(o[k] * inv, 0.0f) & 0xffffu);
+    return;
+  }
+  if (lane == 0) {
+    wm[wave] = m;
+    wl[wave] = l;
+  }
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) wo[wave][lane + 64 * k] = o[k];
+  __syncthreads();
+  const int dd = threadIdx.x;
+  if (dd >= D) return;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kCombineWaves; ++w) M = fmaxf(M, wm[w]);
+  float L = 0.0f, O = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kCombineWaves; ++w) {
+    const float sc = (wm[w] == kNegInf) ? 0.0f : fast_exp2(wm[w] - M);
+    L += sc * wl[w];
+    O += sc * wo[w][dd];
+  }
+  const float val = L > 0.0f ? O / L : 0.0f;
+  dst[dd] = static_cast<uint16_t>(pack_bf16x2(val, 0.0f) & 0xffffu);
 }
 
 template <int D>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t s) {
-  decode_split_kernel<D><<<dim3(static_cast<uint32_t>(p.slots)), dim3(kWaves * 64), 0, s>>>(p);
+  if (p.k_new != nullptr)
+    decode_split_kernel<D, true><<<dim3(static_cast<uint32_t>(p.slots)), dim3(kWaves * 64), 0, s>>>(p);
+  else
+    decode_split_kernel<D, false><<<dim3(static_cast<uint32_t>(p.slots)), dim3(kWaves * 64), 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.slots <= p.n_seq * p.hkv) return e;  // one item per unit: no partials
-  decode_combine_kernel<D><<<dim3(static_cast<uint32_t>(p.n_seq * p.hq)), dim3(D), 0, s>>>(p);
+  decode_combine_kernel<D><<<dim3(static_cast<uint32_t>(p.n_seq * p.hq)), dim3(kCombineWaves * 64), 0, s>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-DecodeShape decode_shape(int32_t n_seq, int32_t hkv, int32_t max_len) {
+DecodeShape decode_shape(int32_t n_seq, int32_t hkv, int32_t max_len, int32_t target) {
   DecodeShape sh{};
   const int64_t units = static_cast<int64_t>(n_seq) * hkv;
   if (units > kDecodePlanUnits) {  // one item per unit
@@ -576,19 +664,19 @@ DecodeShape decode_shape(int32_t n_seq, int32_t hkv, int32_t max_len) {
     return sh;
   }
   // A unit visits at most max_len keys (FA) or ceil(max_len / B) whole blocks
-  // (SA), i.e. fewer than max_len + 128, and gets at most
-  // max(1, min(U * 1024 / total, U / 256)) items: in all at most n_units +
-  // min(1024, total / 256).
-  // The plan keeps the count within the grid: at most 1024 workgroups.
+  // (SA), i.e. fewer than max_len + 128, in items of at least 256 keys.  The
+  // plan keeps the count within max(units, min(target, units + most)).
   const int64_t most = units * (static_cast<int64_t>(max_len) + 127) / kDecodeMinItemKeys;
+  const int64_t t = units + most < target ? units + most : target;
   sh.balanced = 1;
-  sh.slots = units + most < kDecodeTargetItems ? units + most : kDecodeTargetItems;
+  sh.slots = t > units ? t : units;
   return sh;
 }
 
 size_t decode_workspace_bytes(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_dim,
                               int32_t max_len) {
-  const DecodeShape sh = decode_shape(n_seq, hkv, max_len);
+  // sized for the largest target, so it does not depend on the device
+  const DecodeShape sh = decode_shape(n_seq, hkv, max_len, kDecodeMaxItems);
   const size_t units = static_cast<size_t>(n_seq) * hkv;
   if (static_cast<size_t>(sh.slots) <= units) return 0;  // one item per unit: no partials
   const size_t partials = static_cast<size_t>(sh.slots) * (hq / hkv) * (head_dim + 2) * sizeof(float);
@@ -620,6 +708,32 @@ hipError_t decode_scratch(hipStream_t stream, void** ptr) {
   }
   *ptr = addr[dev];
   return hipSuccess;
+}
+
+int32_t decode_target(hipStream_t stream, int32_t head_dim, bool append) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int32_t cache[kMaxDevices][2][2] = {};
+  int dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 512;
+  const int di = head_dim == 128 ? 1 : 0, ai = append ? 1 : 0;
+  std::lock_guard<std::mutex> lock(mu);
+  int32_t& t = cache[dev][di][ai];
+  if (t == 0) {
+    int cus = 0, per_cu = 0;
+    const void* k = di ? (ai ? reinterpret_cast<const void*>(decode_split_kernel<128, true>)
+                             : reinterpret_cast<const void*>(decode_split_kernel<128, false>))
+                       : (ai ? reinterpret_cast<const void*>(decode_split_kernel<64, true>)
+                             : reinterpret_cast<const void*>(decode_split_kernel<64, false>));
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kWaves * 64, 0) != hipSuccess ||
+        cus < 1 || per_cu < 1) {
+      t = 512;  // 256 CUs x 2 workgroups (head_dim 128)
+    } else {
+      t = cus * per_cu < kDecodeMaxItems ? cus * per_cu : kDecodeMaxItems;
+    }
+  }
+  return t;
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {

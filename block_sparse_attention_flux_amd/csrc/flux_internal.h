@@ -39,11 +39,19 @@ struct DecodeParams {
   int32_t block_size;
   int32_t slots;     // workgroups launched (work-item slots)
   int32_t balanced;  // 1: items sized by keys (decode_shape); 0: one item per unit
+  int32_t target;    // items the plan aims at (decode_target)
   int32_t route_heads;                // route decisions per (sequence, layer): 1 or hkv
   int32_t cache_rows;                 // rows per (sequence, kv head) in the caches
   int32_t compact;                    // 1: SA cache of sink rows + a ring of window rows
   int32_t sink_blocks, local_blocks;  // the SA pattern (compact row mapping)
   float scale;
+  // Append fused into the step (full caches only): the row of k_new/v_new
+  // [n_seq][hkv][head_dim] goes to position seqlens[b] - 1 of k_write/v_write
+  // (the caches), and the step reads that key from k_new/v_new.  Null: no append.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_write;
+  uint16_t* v_write;
 };
 
 // Route entry of (request r, layer, kv head g): route[r][layer] when one
@@ -105,17 +113,22 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 
 // Decode work items.  Each (sequence, kv head) unit visits U keys (FA: the
 // sequence's N keys; SA: its mask row's blocks); a call with at most
-// kDecodePlanUnits units cuts them into items of about total / 1024 keys
-// (at least kDecodeMinItemKeys), planned on the device by every workgroup;
-// larger calls take one item per unit.
+// kDecodePlanUnits units cuts them into about `target` items of equal size
+// (at least kDecodeMinItemKeys keys each), planned on the device by every
+// workgroup; larger calls take one item per unit.  The target is the number
+// of split-kernel workgroups the GPU holds at once (one round), at most
+// kDecodeMaxItems, which also sizes the workspace.
 constexpr int32_t kDecodePlanUnits = 1024;
-constexpr int32_t kDecodeTargetItems = 1024;
+constexpr int32_t kDecodeMaxItems = 1024;
 constexpr int32_t kDecodeMinItemKeys = 256;
 struct DecodeShape {
   int64_t slots;     // workgroups to launch (an upper bound on the items)
   int32_t balanced;  // 1: keys-balanced items; 0: one item per unit
 };
-DecodeShape decode_shape(int32_t n_seq, int32_t hkv, int32_t max_len);
+DecodeShape decode_shape(int32_t n_seq, int32_t hkv, int32_t max_len, int32_t target);
+// Resident split-kernel workgroups on the device of `stream` (CUs times the
+// kernel's occupancy), at most kDecodeMaxItems; queried once per device.
+int32_t decode_target(hipStream_t stream, int32_t head_dim, bool append);
 // Bytes of the decode workspace: partials of every slot, then the plan.
 size_t decode_workspace_bytes(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_dim,
                               int32_t max_len);
@@ -125,7 +138,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 constexpr size_t kDecodeScratchBytes = size_t(9) << 20;  // FLUX_DECODE_SCRATCH_BYTES
 // The largest workspace a valid call needs: 1024 slots x 16 query heads per
 // kv head x (128 + 2) floats, plus the plan of 1024 units.
-static_assert(size_t(kDecodeTargetItems) * 16 * (128 + 2) * 4 + size_t(kDecodePlanUnits) * 8 <=
+static_assert(size_t(kDecodeMaxItems) * 16 * (128 + 2) * 4 + size_t(kDecodePlanUnits) * 8 <=
                   kDecodeScratchBytes,
               "the decode scratch must hold the largest workspace");
 hipError_t decode_scratch(hipStream_t stream, void** ptr);

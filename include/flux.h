@@ -282,6 +282,29 @@ flux_status flux_attn_decode(const uint16_t* q, const uint16_t* k_cache,
                              void* stream);
 
 /*
+ * flux_attn_decode_append -- one decode step of one layer with the new
+ * token's K/V row appended in the same launch: the result and the caches
+ * afterwards are those of flux_kv_append(k_new, v_new, seqlens, ..., compact
+ * = 0) followed by flux_attn_decode (the step reads the new key from k_new /
+ * v_new, and one workgroup per (sequence, kv head) stores the row at
+ * position seqlens[b] - 1; sequences with seqlens[b] outside [1, max_len]
+ * get no row, as in flux_kv_append).  Full caches only.
+ * k_new, v_new  [device] bf16 [n_seq][hkv][head_dim], must not alias the
+ *               caches or out; k_cache, v_cache [device] as for
+ *               flux_attn_decode, written at one row per (sequence, kv head).
+ * Everything else, including the workspace, as flux_attn_decode.
+ */
+flux_status flux_attn_decode_append(const uint16_t* q, const uint16_t* k_new,
+                                    const uint16_t* v_new, uint16_t* k_cache, uint16_t* v_cache,
+                                    uint16_t* out, const int32_t* seqlens, int32_t n_seq,
+                                    int32_t max_len, int32_t hq, int32_t hkv, int32_t head_dim,
+                                    float softmax_scale, const uint8_t* route, int32_t n_layers,
+                                    int32_t layer, const int32_t* mask_row_ptr,
+                                    const int32_t* mask_col_idx, int32_t mask_blocks,
+                                    flux_sa_params p, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
  * flux_attn_decode_noalloc -- flux_attn_decode without a workspace argument,
  * for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation).  The

@@ -31,7 +31,7 @@ def declared_symbols(header=HEADER):
 
 def test_exports_every_declared_symbol():
     syms = declared_symbols()
-    assert len(syms) == 19, syms
+    assert len(syms) == 20, syms
     raw = ctypes.CDLL(LIB)
     for s in syms:
         assert hasattr(raw, s), s
@@ -170,6 +170,34 @@ def test_decode_noalloc_validation():
     assert dec(layer=36) == _lib.FLUX_ERR_INVALID_ARG
     assert dec(d=80) == _lib.FLUX_ERR_UNSUPPORTED
     assert dec(hq=64, hkv=2) == _lib.FLUX_ERR_UNSUPPORTED   # 32 query heads per kv head
+
+
+def test_decode_append_validation():
+    """flux_attn_decode_append: flux_attn_decode's checks plus the new rows,
+    which must be given and must not alias the caches or the output."""
+    ws = lib.flux_attn_decode_workspace_size(16, 32, 8, 128, 32768)
+    KC, VC, KN, VN, OUT = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000, 0x50000))
+
+    def dec(**kw):
+        a = dict(q=FAKE, kn=KN, vn=VN, kc=KC, vc=VC, out=OUT, sl=FAKE, n=16, ml=32768, hq=32, hkv=8,
+                 d=128, scale=0.088, route=FAKE, L=36, layer=0, rp=FAKE, ci=FAKE, mb=256,
+                 sa=SA(128, 1, 16), ws=FAKE, wsb=ws, stream=NULL)
+        a.update(kw)
+        return lib.flux_attn_decode_append(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["out"], a["sl"],
+                                           a["n"], a["ml"], a["hq"], a["hkv"], a["d"], a["scale"],
+                                           a["route"], a["L"], a["layer"], a["rp"], a["ci"], a["mb"],
+                                           a["sa"], a["ws"], a["wsb"], a["stream"])
+    assert dec(kn=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(vn=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(kc=NULL) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(kn=KC) == _lib.FLUX_ERR_INVALID_ARG      # new row aliases a cache
+    assert dec(vn=VC) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(out=KC) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(vc=KC) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(q=OUT) == _lib.FLUX_ERR_INVALID_ARG      # out aliases q
+    assert dec(mb=255) == _lib.FLUX_ERR_INVALID_ARG
+    assert dec(d=80) == _lib.FLUX_ERR_UNSUPPORTED
+    assert dec(ws=NULL) == _lib.FLUX_ERR_WORKSPACE
 
 
 def test_decode_validation():

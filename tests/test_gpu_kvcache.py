@@ -95,3 +95,46 @@ def test_compact_sa_decode_matches_full(case):
         if t in check_at:
             ref = oracle.attention_decode(f32(q), f32(kf), f32(vf), sl.cpu().numpy(), False, m, B)
             assert_attn_close(f32(cmp_), ref, f"compact decode step {t}")
+
+
+@pytest.mark.parametrize("case", [
+    # lens, hq, hkv, d, B, s, w, steps
+    ([9000, 130, 1, 2000, 4095], 32, 8, 128, 128, 1, 16, 6),
+    ([700, 64, 63], 8, 2, 64, 64, 1, 3, 4),
+])
+def test_fused_append_matches_append_then_decode(case):
+    """flux_attn_decode_append equals flux_kv_append + flux_attn_decode bit for
+    bit, outputs and caches, step after step, with mixed routes and a sequence
+    whose length falls outside [1, max_len] (no row appended, as kv_append);
+    one step is also checked against the oracle."""
+    lens, hq, hkv, d, B, s, w, steps = case
+    n = len(lens)
+    max_len = max(lens) + steps
+    say(f"fused append {case}")
+    sa = flux.SAParams(B, s, w)
+    g = syn.generator(8383, DEV)
+    kc = syn.normal((n, hkv, max_len, d), g, DEV)
+    vc = syn.normal((n, hkv, max_len, d), g, DEV)
+    kc2, vc2 = kc.clone(), vc.clone()
+    _, rp, ci = flux.build_block_mask(max_len, sa, dense=False)
+    route = torch.tensor([[1, 0], [0, 1]] * (n // 2) + [[1, 1]] * (n % 2), dtype=torch.uint8, device=DEV)
+    base = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    for t in range(steps):
+        sl = base + t + 1
+        if t == steps - 1:
+            sl[1] = max_len + 5   # out of range: no row is appended, the length is clamped
+        q = syn.normal((n, hq, d), g, DEV)
+        kn, vn = syn.normal((n, hkv, d), g, DEV), syn.normal((n, hkv, d), g, DEV)
+        for layer in (0, 1):
+            fused = flux.attn_decode_append(q, kn, vn, kc, vc, sl, route, layer, rp, ci, sa)
+            flux.kv_append(kn, vn, sl, kc2, vc2, max_len, sa)
+            ref_out = flux.attn_decode(q, kc2, vc2, sl, route, layer, rp, ci, sa)
+            torch.cuda.synchronize()
+            assert torch.equal(fused, ref_out), f"step {t} layer {layer}: output differs"
+            assert torch.equal(kc, kc2) and torch.equal(vc, vc2), f"step {t} layer {layer}: caches differ"
+        if t == 2:
+            m = oracle.block_mask(oracle.num_blocks(max_len, B), s, w)
+            lens_t = [int(x) for x in sl.tolist()]
+            fa = [bool(route[b, 1]) for b in range(n)]
+            ref = oracle.attention_decode(f32(q), f32(kc), f32(vc), lens_t, fa, m, B)
+            assert_attn_close(f32(fused), ref, f"fused append step {t}")
