@@ -25,8 +25,6 @@
 //               rule  O = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s.
 #include <mutex>
 
-#include <type_traits>
-
 #include "flux_device.h"
 #include "flux_internal.h"
 
@@ -303,24 +301,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   const uint16_t* kc = p.k_cache + (static_cast<size_t>(b) * p.hkv + g) * cache_head;
   const uint16_t* vc = p.v_cache + (static_cast<size_t>(b) * p.hkv + g) * cache_head;
 
-  // Fused append: the unit's last item writes the new row into the caches;
-  // whichever item visits key N - 1 reads it from k_new / v_new instead, so no
-  // item reads that row from the caches and no workgroup waits for another.
-  const int newk = APPEND && it.app ? N - 1 : -1;
-  const uint16_t* kn_row = nullptr;
-  const uint16_t* vn_row = nullptr;
-  if (APPEND && it.app) {
-    const size_t nrow = (static_cast<size_t>(b) * p.hkv + g) * D;
-    kn_row = p.k_new + nrow;
-    vn_row = p.v_new + nrow;
-    if (it.j == it.s - 1 && wave == 0 && lane < 2 * CH) {
-      const bool isv = lane >= CH;
-      const int c = isv ? lane - CH : lane;
-      const size_t dst = (static_cast<size_t>(b) * p.hkv + g) * cache_head + static_cast<size_t>(N - 1) * D + c * 8;
-      st16((isv ? p.v_write : p.k_write) + dst, ld16((isv ? vn_row : kn_row) + c * 8));
-    }
-  }
-
   // first key position of the chunk that starts at visited index u (wave-uniform)
   auto chunk_key = [&](int u) -> int {
     if (fa) return u;
@@ -328,6 +308,38 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
     const int blk = bi < 64 ? __builtin_amdgcn_readlane(col_lane, bi) : min(max(p.col_idx[rp0 + bi], 0), mrow);
     return blk * B + u % B;
   };
+
+  // Fused append: the new row goes to cache row N - 1 before anything reads
+  // it.  The one wave that visits key N - 1 (FA: visited index N - 1; SA:
+  // inside the row's last block when that is the diagonal block) stores the
+  // row and waits for its own store, so its later load of that row sees it
+  // (no other item and no other wave reads row N - 1).  When no wave visits
+  // it, wave 0 of the unit's last item stores it.
+  if constexpr (APPEND) {
+    if (it.app) {
+      int vi = -1;  // visited index of key N - 1, or -1
+      if (fa) {
+        vi = N - 1;
+      } else if (n_blk > 0) {
+        const int last = (n_blk - 1) < 64 ? __builtin_amdgcn_readlane(col_lane, n_blk - 1)
+                                          : min(max(p.col_idx[rp0 + n_blk - 1], 0), mrow);
+        if (last == mrow) vi = (n_blk - 1) * B + (N - 1) % B;
+      }
+      const bool visit = vi >= u0 && vi < u1;
+      const bool writer = visit ? wave == ((vi - u0) / kChunk) % kWaves
+                                : vi < 0 && it.j == it.s - 1 && wave == 0;
+      if (writer) {
+        if (lane < 2 * CH) {
+          const bool isv = lane >= CH;
+          const int c = isv ? lane - CH : lane;
+          const size_t nrow = (static_cast<size_t>(b) * p.hkv + g) * D + c * 8;
+          const size_t dst = (static_cast<size_t>(b) * p.hkv + g) * cache_head + static_cast<size_t>(N - 1) * D + c * 8;
+          st16((isv ? p.v_write : p.k_write) + dst, ld16((isv ? p.v_new : p.k_new) + nrow));
+        }
+        wait_vmem_all();
+      }
+    }
+  }
   // cache row of key position k: the position itself in a full cache; in a
   // compact cache the sink rows come first and every later block has its
   // ring slot (block j at rows sink*B + (j % local)*B).  A 32-key chunk never
@@ -371,40 +383,25 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
     k0 = chunk_key(u);
     limit = min(k0 + min(u1 - u, kChunk), N);
     const int row0 = cache_row(k0) - k0;  // row of key k is row0 + k within this chunk
-    // Rows come from the caches, except the appended key's, which comes from
-    // k_new / v_new (APPEND only: a per-lane choice of the row address; a
-    // wave-uniform branch to a second copy of the loads for the one chunk
-    // holding that key measured slower, it spilled registers).
-    auto rows = [&](auto with_new) {
-      constexpr bool kNew = decltype(with_new)::value;
-      auto krow = [&](int key) {
-        return kNew && key == newk ? kn_row : kc + static_cast<size_t>(row0 + key) * D;
-      };
-      auto vrow = [&](int key) {
-        return kNew && key == newk ? vn_row : vc + static_cast<size_t>(row0 + key) * D;
-      };
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int key = k0 + mt * 16 + l16;
+    for (int mt = 0; mt < 2; ++mt) {
+      const int key = k0 + mt * 16 + l16;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
-          kr[mt][ks] = key < limit ? ld16_stream(krow(key) + ks * 32 + quarter * 8) : u32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        kr[mt][ks] = key < limit ? ld16_stream(kc + static_cast<size_t>(row0 + key) * D + ks * 32 + quarter * 8)
+                                 : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < VQC; ++j) {
+      const int id = lane + 64 * j;
+      const int c = id % CH, qd = id / CH;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int key = k0 + qd * 4 + kk;
+        vr[j][kk] = key < limit ? ld16_stream(vc + static_cast<size_t>(row0 + key) * D + c * 8)
+                                : u32x4{0, 0, 0, 0};
       }
-#pragma unroll
-      for (int j = 0; j < VQC; ++j) {
-        const int id = lane + 64 * j;
-        const int c = id % CH, qd = id / CH;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int key = k0 + qd * 4 + kk;
-          vr[j][kk] = key < limit ? ld16_stream(vrow(key) + c * 8) : u32x4{0, 0, 0, 0};
-        }
-      }
-    };
-    if constexpr (APPEND)
-      rows(std::true_type{});
-    else
-      rows(std::false_type{});
+    }
   };
 
   auto compute_chunk = [&](const KRegs& kr, const VRegs& vr, int k0, int limit) {

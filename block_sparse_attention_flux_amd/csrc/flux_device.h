@@ -34,6 +34,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// Wait until every vector memory operation this wave issued has completed
+// (loads returned, stores acknowledged): s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // 16-byte global load / store of raw bits.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);

@@ -89,7 +89,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 //           covers exactly one block, and the two groups of a 32-lane pass
 //           (quads 2i, 2i + 1, the same j) land 128 bytes apart modulo 256,
 //           i.e. on disjoint halves of the banks.
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // Loads of one K or V tile into LDS by NT threads.  Load j of thread tid
 // fills LDS slot s = j*NT + tid (16 bytes, lane-linear per wave instruction);

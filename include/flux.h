@@ -285,9 +285,9 @@ flux_status flux_attn_decode(const uint16_t* q, const uint16_t* k_cache,
  * flux_attn_decode_append -- one decode step of one layer with the new
  * token's K/V row appended in the same launch: the result and the caches
  * afterwards are those of flux_kv_append(k_new, v_new, seqlens, ..., compact
- * = 0) followed by flux_attn_decode (the step reads the new key from k_new /
- * v_new, and one workgroup per (sequence, kv head) stores the row at
- * position seqlens[b] - 1; sequences with seqlens[b] outside [1, max_len]
+ * = 0) followed by flux_attn_decode (per (sequence, kv head), the one wave
+ * that reads key seqlens[b] - 1 first stores the new row at that position
+ * and waits for the store; sequences with seqlens[b] outside [1, max_len]
  * get no row, as in flux_kv_append).  Full caches only.
  * k_new, v_new  [device] bf16 [n_seq][hkv][head_dim], must not alias the
  *               caches or out; k_cache, v_cache [device] as for
