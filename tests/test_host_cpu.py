@@ -112,3 +112,48 @@ def test_build_flags_of_the_package_sources():
     assert bench.build_flags("block_sparse_attention_flux_amd/csrc/prefill.hip") == \
         ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
     assert bench.build_flags("block_sparse_attention_flux_amd/csrc/decode.hip") == []
+
+
+def _bench():
+    import bench
+    return bench
+
+
+@pytest.mark.parametrize("S,fa,B,s,w", [(512, True, 64, 1, 2), (512, False, 64, 1, 2), (1000, False, 128, 3, 2),
+                                        (581, True, 64, 0, 3), (300, False, 128, 0, 8), (129, False, 64, 1, 1)])
+def test_prefill_work_counts_against_brute_force(S, fa, B, s, w):
+    """The three work counts of bench.prefill_work, recounted one query row,
+    one key and one (wave, tile) pair at a time from the oracle's mask."""
+    import numpy as np
+    import oracle
+    d, hq, bn = 64, 2, 32
+    nb = oracle.num_blocks(S, B)
+    m = oracle.block_mask(nb, s, w)
+    allowed = oracle.allowed_matrix(np.arange(S), S, fa, m, B)
+    blocks = int(np.tril(np.ones((nb, nb))).sum()) if fa else int(m.sum())
+    tiles = 0
+    for t in range(nb):
+        cols = range(t + 1) if fa else [j for j in range(nb) if m[t, j]]
+        starts = [j * B + k * bn for j in cols for k in range(B // bn)]
+        for wi in range(B // bn):
+            first_row = t * B + wi * bn
+            if first_row < S:
+                tiles += sum(1 for st in starts if st <= first_row + bn - 1 and st < min(t * B + B, S))
+    got = _bench().prefill_work(S, fa, B, s, w, d, hq, bn)
+    assert got["causal"] == allowed.sum() * 4 * d * hq
+    assert got["blocks"] == blocks * 4 * B * B * d * hq
+    assert got["tiles"] == tiles * 4 * bn * bn * d * hq
+
+
+def test_prefill_work_at_32k():
+    """32768 tokens, 32 q heads, d 128, B 128: FA 32896 blocks, SA 4216 blocks
+    (1 sink + 16 window blocks); every diagonal block runs 10 of its 16
+    (wave, tile) pairs."""
+    b = _bench()
+    blk = 4.0 * 128 * 128 * 128 * 32
+    fa = b.prefill_work(32768, True, 128, 1, 16, 128, 32)
+    sa = b.prefill_work(32768, False, 128, 1, 16, 128, 32)
+    assert fa["blocks"] == 32896 * blk and sa["blocks"] == 4216 * blk
+    assert fa["tiles"] == (32896 - 256) * blk + 256 * blk * 10 / 16
+    assert sa["tiles"] == (4216 - 256) * blk + 256 * blk * 10 / 16
+    assert fa["causal"] == 32768 * 32769 // 2 * 4.0 * 128 * 32
