@@ -478,13 +478,16 @@ struct TileList {
   }
 };
 
-// Workgroup -> (kv group, query block heaviest first, request, head slot).
+// Workgroup -> (kv group, request, query block heaviest first, head slot).
 // Workgroup ids are dealt to the 8 XCDs round-robin (id % 8).  With one route
 // decision per layer the order is XCD-major: each XCD works through whole KV
-// head groups, so consecutive work items share an XCD's L2.  With one
-// decision per kv head that would leave the XCDs that drew FA groups running
-// long after the others, so there each XCD's share cycles through all kv
-// groups instead (heaviest query blocks still first).
+// head groups, one request at a time, so the workgroups an XCD holds at once
+// are the query heads of a few neighbouring query blocks of one request and
+// share its K/V in the XCD's L2 (with the requests interleaved instead, a
+// packed batch of long prompts spread them over every request's K/V).  With
+// one decision per kv head the XCD-major order would leave the XCDs that drew
+// FA groups running long after the others, so there each XCD's share cycles
+// through all kv groups instead (heaviest query blocks still first).
 __device__ __forceinline__ void decode_work(int n_slots, int n_req, int n_qt, int hkv, bool by_head,
                                             int& slot, int& req, int& t, int& g) {
   const int G = gridDim.x, bid = blockIdx.x;
@@ -503,10 +506,10 @@ __device__ __forceinline__ void decode_work(int n_slots, int n_req, int n_qt, in
   w = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
   slot = w % n_slots;
   w /= n_slots;
-  req = w % n_req;
-  w /= n_req;
   t = n_qt - 1 - (w % n_qt);
-  g = w / n_qt;
+  w /= n_qt;
+  req = w % n_req;
+  g = w / n_req;
 }
 
 // SOFT: the soft-routed forward, O = r FA + (1 - r) SA with r per (request,
