@@ -485,8 +485,9 @@ def dynamic_mask(flux, q, k, v, cu, S, wl, sa, sa_ms, stream, log):
 def soft_routing(flux, q, k, v, cu, S, row_ptr, col_idx, sa, fa_ms, sa_ms, fa_flops, sa_flops, stream,
                  log):
     """The soft-routed forward r FA + (1 - r) SA of one 32K layer in one pass,
-    against the FA and SA layers run separately (the soft pass shares S and the
-    K/V tiles of the SA blocks with the FA branch)."""
+    against the FA and SA layers run separately and against the FA layer
+    alone (the pass visits the SA blocks first, parks the weighted SA output,
+    and completes FA with the same softmax state: FA's work)."""
     import torch
 
     r = torch.tensor([[0.5, 0.5]], dtype=torch.float32, device=q.device)
@@ -502,7 +503,8 @@ def soft_routing(flux, q, k, v, cu, S, row_ptr, col_idx, sa, fa_ms, sa_ms, fa_fl
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     log(f"soft routing: one pass {ms:.3f} ms vs FA + SA layers {fa_ms + sa_ms:.3f} ms")
-    return {"soft_pass_ms": round(ms, 4), "fa_plus_sa_ms": round(fa_ms + sa_ms, 4),
+    return {"soft_pass_ms": round(ms, 4), "fa_plus_sa_ms": round(fa_ms + sa_ms, 4), "fa_layer_ms": round(fa_ms, 4),
+            "vs_fa_layer": round(ms / fa_ms, 3),
             "speedup_vs_two_layers": round((fa_ms + sa_ms) / ms, 3),
             "tflops_fa_plus_sa_work": round((fa_flops + sa_flops) / ms / 1e9, 1)}
 

@@ -186,15 +186,14 @@ struct TileLoader {
 // so every row is spread over the 4 lanes l%16 + 16g.  O^T is D/16 d tiles x
 // 2 row tiles.  Every MFMA of a tile is independent of the other chains: 4
 // accumulators of K Q^T (4 dependent k-steps each for d 128), and each O^T
-// tile takes one 32-key k-step.  NACC online-softmax states (O, running max,
-// running sum) share the wave's Q and S: one for routed layers, two (FA and
-// SA) for the soft-routed forward.
+// tile takes one 32-key k-step.  One online-softmax state (O, running max,
+// running sum) per row.
 //
 // The k index of the P V product runs over the tile's 32 keys in the order
 // the S^T layout leaves them in a lane: k = 8g + e is key 16(e/4) + 4g + e%4,
 // for P (the B operand, straight from the exponentials) and for V^T (the A
 // operand, two transpose reads of 4 keys each) alike.
-template <int D, int BN, int NACC = 1>
+template <int D, int BN>
 struct WaveAttn {
   static_assert(BN == 32, "one 32-key k-step of P V per tile");
   static constexpr int KS = D / 32;   // k-steps of K Q^T
@@ -204,8 +203,8 @@ struct WaveAttn {
   static constexpr int PK = 8;         // packed bf16 pairs of P per lane (2 rows x 4)
 
   bf16x8 qreg[2][KS];
-  f32x4 oacc[NACC][2][DT];
-  float m_run[NACC][2], l_run[NACC][2], cs;
+  f32x4 oacc[2][DT];
+  float m_run[2], l_run[2], cs;
   int l16, grp, wrow0, krd, vrd_e, vrd_o;
 
   __device__ __forceinline__ void init(const uint16_t* q, int tok0, int hq, int head, int q_row0,
@@ -227,14 +226,12 @@ struct WaveAttn {
     }
     cs = scale * kLog2e;  // scores -> log2 domain
 #pragma unroll
-    for (int a = 0; a < NACC; ++a)
+    for (int c = 0; c < 2; ++c) {
+      m_run[c] = kNegInf;
+      l_run[c] = 0.0f;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        m_run[a][c] = kNegInf;
-        l_run[a][c] = 0.0f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[a][c][dt] = f32x4{};
-      }
+      for (int dt = 0; dt < DT; ++dt) oacc[c][dt] = f32x4{};
+    }
     // K operand: key row l%16 (+16 kt), chunk 4ks + g: one base, constant offsets
     krd = (l16 * KROW + grp) * 16;
     // V^T operand (transpose read): the 16 lanes of group g read the 128-byte
@@ -301,7 +298,6 @@ struct WaveAttn {
   // rows whose max grew past the slack move their reference (rescaling their
   // O and sum), and the exponentials are redone; rows that did not move get
   // bit-identical P, so each row's result depends on its own data only.
-  template <int A = 0>
   __device__ __forceinline__ void softmax(f32x4 (&s)[2][2], int kst, uint32_t (&pk)[PK]) {
     if (kst + BN - 1 > wrow0) {  // tile crosses the diagonal: causal mask
 #pragma unroll
@@ -315,9 +311,9 @@ struct WaveAttn {
           }
     }
     float ps[2] = {0.0f, 0.0f};
-    bool slow = __ballot(m_run[A][0] == kNegInf || m_run[A][1] == kNegInf) != 0;  // wave-uniform
+    bool slow = __ballot(m_run[0] == kNegInf || m_run[1] == kNegInf) != 0;  // wave-uniform
     if (!slow) {
-      exps(s, m_run[A], pk, ps);
+      exps(s, m_run, pk, ps);
       slow = __ballot(!(ps[0] + ps[1] <= kSumLimit)) != 0;
     }
     if (slow) {
@@ -331,26 +327,26 @@ struct WaveAttn {
 #pragma unroll
           for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kt][c][r]);
         mxs[c] = max_quarters(max_halves(mx)) * cs;
-        grow[c] = mxs[c] > m_run[A][c] + kRescaleSlack;
+        grow[c] = mxs[c] > m_run[c] + kRescaleSlack;
       }
       if (__ballot(grow[0] || grow[1]) != 0) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const float m_new = grow[c] ? mxs[c] : m_run[A][c];
+          const float m_new = grow[c] ? mxs[c] : m_run[c];
           const float alpha =
-              !grow[c] ? 1.0f : (m_run[A][c] == kNegInf) ? 0.0f : fast_exp2(m_run[A][c] - m_new);
-          l_run[A][c] *= alpha;
+              !grow[c] ? 1.0f : (m_run[c] == kNegInf) ? 0.0f : fast_exp2(m_run[c] - m_new);
+          l_run[c] *= alpha;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) oacc[A][c][dt] *= alpha;
-          m_run[A][c] = m_new;
+          for (int dt = 0; dt < DT; ++dt) oacc[c][dt] *= alpha;
+          m_run[c] = m_new;
         }
       }
-      const float mu[2] = {m_run[A][0] == kNegInf ? 0.0f : m_run[A][0],
-                           m_run[A][1] == kNegInf ? 0.0f : m_run[A][1]};
+      const float mu[2] = {m_run[0] == kNegInf ? 0.0f : m_run[0],
+                           m_run[1] == kNegInf ? 0.0f : m_run[1]};
       exps(s, mu, pk, ps);
     }
-    l_run[A][0] += ps[0];
-    l_run[A][1] += ps[1];
+    l_run[0] += ps[0];
+    l_run[1] += ps[1];
   }
 
   // 4 keys (quad 4kt + g) x 16 d (tile dt) of V^T, transposed: element e of
@@ -361,7 +357,6 @@ struct WaveAttn {
   }
 
   // O^T += V^T P^T for the V tile at vl
-  template <int A = 0>
   __device__ __forceinline__ void pv(const lds_u8* vl, const uint32_t (&pk)[PK]) {
     s16x8 vop[DT];
 #pragma unroll
@@ -374,11 +369,44 @@ struct WaveAttn {
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        oacc[A][c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[dt]), b[c],
-                                                                 oacc[A][c][dt], 0, 0, 0);
+        oacc[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[dt]), b[c],
+                                                                 oacc[c][dt], 0, 0, 0);
   }
 
-  // O = w0 O_0 / l_0 (+ w1 O_1 / l_1), staged through this wave's LDS slice
+  // Soft-routed forward: w O / l of this wave's rows (the weighted SA
+  // output) parked in `out` as bf16, straight from the accumulator layout
+  // (lane l: d 16dt + 4(l/16) .. +3 of rows 16c + l%16), 8 bytes per store;
+  // unpark() reads the same bytes back into the same lanes.
+  __device__ __forceinline__ uint16_t* parked_at(uint16_t* out, int tok0, int hq, int head, int c,
+                                                 int dt) const {
+    return out + (static_cast<size_t>(tok0 + wrow0 + 16 * c + l16) * hq + head) * D + 16 * dt + 4 * grp;
+  }
+  __device__ __forceinline__ void park(uint16_t* out, int tok0, int hq, int head, int S, float w) const {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const float lt = sum_quarters(sum_halves(l_run[c]));
+      const float inv = (lt > 0.0f ? 1.0f / lt : 0.0f) * w;
+      if (wrow0 + 16 * c + l16 < S) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<u32x2*>(parked_at(out, tok0, hq, head, c, dt)) =
+              u32x2{pack_bf16x2(oacc[c][dt][0] * inv, oacc[c][dt][1] * inv),
+                    pack_bf16x2(oacc[c][dt][2] * inv, oacc[c][dt][3] * inv)};
+      }
+    }
+  }
+  __device__ __forceinline__ void unpark(uint16_t* out, int tok0, int hq, int head, int S,
+                                         u32x2 (&pk)[2][DT]) const {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bool ok = wrow0 + 16 * c + l16 < S;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        pk[c][dt] = ok ? *reinterpret_cast<const u32x2*>(parked_at(out, tok0, hq, head, c, dt)) : u32x2{0, 0};
+    }
+  }
+
+  // O = w O / l (+ the parked values), staged through this wave's LDS slice
   // (32 rows of D bf16, free once the tile loop has ended) so that every
   // global store writes 16 bytes per lane and whole rows per instruction.
   // The slice is written in the accumulator layout (lane l: d 16dt + 4(l/16)
@@ -386,25 +414,25 @@ struct WaveAttn {
   // are XOR-swizzled by the row (D 128: row & 15; D 64: (row >> 1) & 7) so
   // both passes are free of bank conflicts.
   __device__ __forceinline__ void store(uint16_t* out, int tok0, int hq, int head, int S, lds_u8* stage,
-                                        int lane, float w0 = 1.0f, float w1 = 0.0f) const {
+                                        int lane, float w = 1.0f, const u32x2 (*parked)[DT] = nullptr) const {
     constexpr int CH = D / 8;  // 16-byte chunks per row
     auto swz = [](int r) { return CH == 16 ? (r & 15) : ((r >> 1) & 7); };
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      float inv[NACC];
-#pragma unroll
-      for (int a = 0; a < NACC; ++a) {
-        const float lt = sum_quarters(sum_halves(l_run[a][c]));
-        inv[a] = (lt > 0.0f ? 1.0f / lt : 0.0f) * (a == 0 ? w0 : w1);
-      }
+      const float lt = sum_quarters(sum_halves(l_run[c]));
+      const float inv = (lt > 0.0f ? 1.0f / lt : 0.0f) * w;
       const int r = 16 * c + l16;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         float o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o[e] = oacc[0][c][dt][e] * inv[0];
-          if (NACC > 1) o[e] = __builtin_fmaf(oacc[NACC - 1][c][dt][e], inv[NACC - 1], o[e]);
+        for (int e = 0; e < 4; ++e) o[e] = oacc[c][dt][e] * inv;
+        if (parked != nullptr) {
+          const uint32_t a = parked[c][dt][0], b = parked[c][dt][1];
+          o[0] += u32_as_f32(a << 16);
+          o[1] += u32_as_f32(a & 0xffff0000u);
+          o[2] += u32_as_f32(b << 16);
+          o[3] += u32_as_f32(b & 0xffff0000u);
         }
         const int chunk = 2 * dt + (grp >> 1);
         *reinterpret_cast<lds_u32x2*>(stage + r * (D * 2) + ((chunk ^ swz(r)) * 16) + (grp & 1) * 8) =
@@ -478,6 +506,56 @@ struct TileList {
   }
 };
 
+// Tile order of the soft-routed forward: first the tiles of the blocks in the
+// query block's CSR row (SA), then those of the other causal blocks 0 .. t in
+// increasing order (what FA adds), so one softmax state yields SA after the
+// first phase and FA after both.  The CSR row is trusted to be increasing;
+// its columns are clamped into [0, t] as everywhere (repeats count once).
+// start() must be called with n = 0, 1, 2, ... in order: the second phase
+// walks the complement with a cursor into the row.
+template <int BM, int BN>
+struct SoftOrder {
+  static constexpr int TPB = BM / BN;
+  TileList<BM, BN> sa;
+  int n_sa, n_tiles, n_row, t, cb, cp;
+  __device__ __forceinline__ int col(int i) const { return sa.start(i * TPB) / BM; }  // clamped
+  __device__ __forceinline__ void init(const PrefillParams& p, int qt, int rb, int re, int lane, int q_end) {
+    t = qt;
+    n_row = max(re - rb, 0);
+    sa.init(p, qt, false, rb, re, lane);
+    sa.trim(q_end);
+    n_sa = sa.n_tiles;
+    int distinct = 0, prev = -1;
+    for (int i = 0; i < n_row; ++i) {
+      const int c = col(i);
+      distinct += c != prev;
+      prev = c;
+    }
+    int comp = (t + 1 - distinct) * TPB;
+    if (prev != t) comp -= TPB - (q_end - t * BM + BN - 1) / BN;  // block t is FA-only: trim it
+    n_tiles = n_sa + comp;
+    cb = -1;
+    cp = 0;
+  }
+  __device__ __forceinline__ int start(int n) {
+    if (n < n_sa) return sa.start(n);
+    const int k = n - n_sa;
+    if (k % TPB == 0) {  // next block that is not in the row
+      int b = cb + 1;
+      for (;;) {
+        while (cp < n_row && col(cp) < b) ++cp;
+        if (cp < n_row && col(cp) == b) {
+          ++b;
+          continue;
+        }
+        break;
+      }
+      cb = b;
+    }
+    return cb * BM + (k % TPB) * BN;
+  }
+};
+
 // Workgroup -> (kv group, request, query block heaviest first, head slot).
 // Workgroup ids are dealt to the 8 XCDs round-robin (id % 8).  With one route
 // decision per layer the order is XCD-major: each XCD works through whole KV
@@ -513,9 +591,11 @@ __device__ __forceinline__ void decode_work(int n_slots, int n_req, int n_qt, in
 }
 
 // SOFT: the soft-routed forward, O = r FA + (1 - r) SA with r per (request,
-// layer): every tile up to the diagonal feeds the FA state, and the tiles of
-// the blocks in the query block's CSR row (a subset) also feed the SA state,
-// from the same S and the same K/V tiles in LDS.
+// layer), with one softmax state (SoftOrder): the SA tiles come first; after
+// the last of them every wave parks (1 - r) O / l of its rows in `out`; the
+// same state then runs over FA's other causal tiles, and the result r O / l
+// plus the parked value is written.  The SA blocks being a subset of FA's,
+// this is FA's work alone, at the routed kernel's occupancy.
 template <int D, int BM, int BN, int OCC, bool SOFT = false>
 __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParams p) {
   constexpr int NT = BM * 2;
@@ -564,22 +644,25 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   const int q_end = min(q0 + BM, S);
 
   TileList<BM, BN> tiles;
-  tiles.init(p, t, fa, rb, re, lane);
-  tiles.trim(q_end);
-  // SOFT: the SA blocks of this query block, walked in step with the FA tiles
-  TileList<BM, BN> sa_tiles;
-  int sa_next = 0, sa_blocks = 0;
+  SoftOrder<BM, BN> soft;
+  int n_tiles;
   if constexpr (SOFT) {
-    sa_tiles.init(p, t, false, rb, re, lane);
-    sa_tiles.trim(q_end);
-    sa_blocks = (sa_tiles.n_tiles + TileList<BM, BN>::TPB - 1) / TileList<BM, BN>::TPB;
+    soft.init(p, t, rb, re, lane, q_end);
+    n_tiles = soft.n_tiles;
+  } else {
+    tiles.init(p, t, fa, rb, re, lane);
+    tiles.trim(q_end);
+    n_tiles = tiles.n_tiles;
   }
   Loader ld;
   ld.init(p.k, p.v, tok0, p.hkv, g, S, tid);
-  WaveAttn<D, BN, SOFT ? 2 : 1> wa;
-  wa.init(p.q, tok0, p.hq, head, q0 + wave * 32, S, p.scale, lane);  // in flight with the first tile
-  const int n_tiles = tiles.n_tiles;
-  const int n_mine = tiles.visible(q0 + wave * 32, S);
+  WaveAttn<D, BN> wa;
+  const int wrow0 = q0 + wave * 32;
+  wa.init(p.q, tok0, p.hq, head, wrow0, S, p.scale, lane);  // in flight with the first tile
+  // routed layers: the tiles are in increasing order, so a wave's are a prefix
+  const int n_mine = SOFT ? 0 : tiles.visible(wrow0, S);
+  float r_fa = 1.0f;  // SOFT: the FA weight of this request and layer
+  if constexpr (SOFT) r_fa = p.rsoft[static_cast<int64_t>(req) * p.n_layers + p.layer];
 
   // Step n computes tile n from one buffer pair while tile n+1 loads into the
   // other; the loop is unrolled by two so that each step names its buffers.
@@ -589,53 +672,66 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   auto step = [&](int n, const lds_u8* kc, const lds_u8* vc, lds_u8* kn, lds_u8* vn) {
     int kst_next = 0;
     if (n + 1 < n_tiles) {
-      // tiles of one mask block are contiguous: look the column up only at a block's first tile
-      kst_next = (n + 1) % TileList<BM, BN>::TPB != 0 ? kst + BN : tiles.start(n + 1);
+      if constexpr (SOFT) {
+        kst_next = soft.start(n + 1);
+      } else {
+        // tiles of one mask block are contiguous: look the column up only at a block's first tile
+        kst_next = (n + 1) % TileList<BM, BN>::TPB != 0 ? kst + BN : tiles.start(n + 1);
+      }
       ld.issue(false, kst_next, kn);
       ld.issue(true, kst_next, vn);
     }
-    bool in_sa = false;
-    if constexpr (SOFT) {  // is this tile's block the next block of the SA row?
-      const int blk = kst / BM;
-      while (sa_next < sa_blocks && sa_tiles.start(sa_next * TileList<BM, BN>::TPB) / BM < blk)
-        ++sa_next;
-      in_sa = sa_next < sa_blocks && sa_tiles.start(sa_next * TileList<BM, BN>::TPB) / BM == blk;
-    }
-    if (n < n_mine) {
+    // SOFT tiles are not in key order: a wave computes the tiles that start
+    // at or before its last row
+    const bool mine = SOFT ? (wrow0 < S && kst <= wrow0 + 31) : n < n_mine;
+    if (mine) {
       f32x4 sacc[2][2];
       uint32_t pk[WaveAttn<D, BN>::PK];
       wa.qk(kc, sacc);
       wa.softmax(sacc, kst, pk);
       wa.pv(vc, pk);
-      if constexpr (SOFT) {
-        if (in_sa) {
-          wa.template softmax<1>(sacc, kst, pk);
-          wa.template pv<1>(vc, pk);
-        }
-      }
     }
     kst = kst_next;
     wait_vmem_all();
     __syncthreads();
   };
+  // tiles [n0, n1): tile n lives in buffer pair n & 1
+  auto run = [&](int n0, int n1) {
+    int n = n0;
+    if (n < n1 && (n & 1)) step(n++, k1, v1, k0, v0);
+    for (; n < n1; n += 2) {
+      step(n, k0, v0, k1, v1);
+      if (n + 1 >= n1) break;
+      step(n + 1, k1, v1, k0, v0);
+    }
+  };
   if (n_tiles > 0) {
-    kst = tiles.start(0);
+    if constexpr (SOFT) {
+      kst = soft.start(0);
+    } else {
+      kst = tiles.start(0);
+    }
     ld.issue(false, kst, k0);
     ld.issue(true, kst, v0);
     wait_vmem_all();
     __syncthreads();
-    for (int n = 0; n < n_tiles; n += 2) {
-      step(n, k0, v0, k1, v1);
-      if (n + 1 >= n_tiles) break;
-      step(n + 1, k1, v1, k0, v0);
-    }
+  }
+  if constexpr (SOFT) {
+    run(0, soft.n_sa);                                         // SA's tiles
+    wa.park(p.out, tok0, p.hq, head, S, 1.0f - r_fa);          // (1 - r) SA of these rows
+    run(soft.n_sa, n_tiles);                                   // FA's other tiles
+  } else {
+    run(0, n_tiles);
   }
   // O goes out through LDS: wave w stages its rows in tile array w (every
   // wave has passed the loop's last barrier, so no tile is read any more)
   lds_u8* const stage = wave == 0 ? k0 : wave == 1 ? k1 : wave == 2 ? v0 : v1;
   if constexpr (SOFT) {
-    const float r = p.rsoft[static_cast<int64_t>(req) * p.n_layers + p.layer];
-    wa.store(p.out, tok0, p.hq, head, S, stage, lane, r, 1.0f - r);
+    // the parked SA part: written by this wave's own lanes at least one
+    // vmcnt(0) wait ago (each step ends with one)
+    u32x2 parked[2][WaveAttn<D, BN>::DT];
+    wa.unpark(p.out, tok0, p.hq, head, S, parked);
+    wa.store(p.out, tok0, p.hq, head, S, stage, lane, r_fa, parked);
   } else {
     wa.store(p.out, tok0, p.hq, head, S, stage, lane);
   }
@@ -645,13 +741,12 @@ template <int D, int BM>
 hipError_t launch_typed(const PrefillParams& p, hipStream_t s) {
   const int n_qt = (p.max_seqlen + BM - 1) / BM;
   const int64_t grid = static_cast<int64_t>(n_qt) * p.hq * p.n_req;
-  if (p.rsoft != nullptr) {  // two O accumulators: built for 2 waves per SIMD
-    prefill_kernel<D, BM, kBN, 2, true><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
-  } else {
-    // 64-row blocks: 2-wave workgroups whose tiles hold LDS for 2 waves per SIMD
-    constexpr int occ = BM == 128 ? kOcc : 2;
+  // 64-row blocks: 2-wave workgroups whose tiles hold LDS for 2 waves per SIMD
+  constexpr int occ = BM == 128 ? kOcc : 2;
+  if (p.rsoft != nullptr)
+    prefill_kernel<D, BM, kBN, occ, true><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
+  else
     prefill_kernel<D, BM, kBN, occ><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
-  }
   return hipGetLastError();
 }
 
