@@ -455,50 +455,78 @@ struct WaveAttn {
 // wave keeps the row's first 64 columns one per lane (read with one load,
 // picked with readlane), so finding a tile's start needs no LDS and no
 // barrier; later columns, rare, are read from memory.
+//
+// SA visits its diagonal block first when the row ends with it (the static
+// and the content-aware masks always do): the first tile is then known from
+// the block index alone, so its K/V loads leave with the Q loads instead of
+// waiting for the row's columns; check_diag() then confirms the guess from
+// the columns (otherwise the row is visited in its own order).  The order of
+// the tiles does not change the result beyond rounding (online softmax).
 template <int BM, int BN>
 struct TileList {
   static constexpr int TPB = BM / BN;  // key tiles per mask block
   const int32_t* col_idx;
-  int rp0, n_tiles, t, col_lane;
-  bool fa;
-  // rb, re: the mask row's CSR bounds (read by the caller beside the route)
-  __device__ __forceinline__ void init(const PrefillParams& p, int qt, bool is_fa, int rb, int re, int lane) {
+  int rp0, n_row, n_tiles, n_diag, t, col_lane;
+  bool fa, diag_first;
+  // rb, re: the mask row's CSR bounds (read by the caller beside the route);
+  // q_end: one past the query block's last row
+  __device__ __forceinline__ void init(const PrefillParams& p, int qt, bool is_fa, int rb, int re, int lane,
+                                       int q_end) {
     fa = is_fa;
     t = qt;
     col_idx = p.col_idx;
     rp0 = rb;
     col_lane = 0;
-    n_tiles = 0;
-    if (!fa) {
-      const int n_blocks = max(re - rb, 0);
-      col_lane = lane < n_blocks ? col_idx[rp0 + lane] : 0;  // clamped when read
-      n_tiles = n_blocks * TPB;
-    }
-  }
-  // tiles of the query block ending at q_end (FA: up to the diagonal; SA:
-  // the CSR row without tiles that start past the block's last row)
-  __device__ __forceinline__ void trim(int q_end) {
+    n_row = 0;
+    diag_first = false;
+    n_diag = min(TPB, (q_end - t * BM + BN - 1) / BN);  // tiles of the diagonal block before q_end
     if (fa) {
       n_tiles = (q_end + BN - 1) / BN;
       return;
     }
-    while (n_tiles > 0 && start(n_tiles - 1) >= q_end) --n_tiles;
+    n_row = max(re - rb, 0);
+    col_lane = lane < n_row ? col_idx[rp0 + lane] : 0;  // clamped when read
+    diag_first = n_row > 0;  // a guess until check_diag()
+    n_tiles = diag_first ? (n_row - 1) * TPB + n_diag : 0;
   }
-  __device__ __forceinline__ int start(int n) const {
-    if (fa) return n * BN;
-    const int bi = n / TPB;
+  __device__ __forceinline__ int col(int i) const {
     int c;
-    if (bi < 64) {
-      c = __builtin_amdgcn_readlane(col_lane, bi);
+    if (i < 64) {
+      c = __builtin_amdgcn_readlane(col_lane, i);
     } else {
       // made scalar inside the branch, so the wait for this load stays on
       // this (rare) path and never covers the tile loads in flight
-      c = __builtin_amdgcn_readfirstlane(col_idx[rp0 + bi]);
+      c = __builtin_amdgcn_readfirstlane(col_idx[rp0 + i]);
     }
-    return min(max(c, 0), t) * BM + (n % TPB) * BN;
+    return min(max(c, 0), t);
   }
-  // tiles a wave whose first row is wrow0 must see (up to its last row)
-  __device__ __forceinline__ int visible(int wrow0, int S) const {
+  // SA: keep the diagonal-first order if the row's last column is the
+  // diagonal block; otherwise fall back to the row's order, without the
+  // tiles that start past the block's last row.  Returns true if it changed.
+  __device__ __forceinline__ bool check_diag() {
+    if (fa || !diag_first || col(n_row - 1) == t) return false;
+    diag_first = false;
+    n_tiles = n_row * TPB;
+    while (n_tiles > 0 && start(n_tiles - 1) >= t * BM + n_diag * BN) --n_tiles;
+    return true;
+  }
+  __device__ __forceinline__ int start(int n) const {
+    if (fa) return n * BN;
+    if (diag_first) {
+      if (n < n_diag) return t * BM + n * BN;
+      n -= n_diag;  // then the row's other blocks, in order
+    }
+    return col(n / TPB) * BM + (n % TPB) * BN;
+  }
+  // start of tile n + 1 given that tile n starts at kst: the tiles of a block
+  // are contiguous, so a column is looked up only at a block's first tile
+  __device__ __forceinline__ int next_start(int n, int kst) const {
+    const int k = n + 1 - (diag_first ? n_diag : 0);  // < 0: still inside the diagonal block
+    return (fa || k < 0 || k % TPB != 0) ? kst + BN : start(n + 1);
+  }
+  // does the wave whose first row is wrow0 compute tile n (does it start at
+  // or before the wave's last row)?
+  __device__ __forceinline__ int visible_prefix(int wrow0, int S) const {  // sorted orders
     if (wrow0 >= S) return 0;
     int n = n_tiles;
     while (n > 0 && start(n - 1) > wrow0 + 31) --n;
@@ -518,12 +546,12 @@ struct SoftOrder {
   static constexpr int TPB = BM / BN;
   TileList<BM, BN> sa;
   int n_sa, n_tiles, n_row, t, cb, cp;
-  __device__ __forceinline__ int col(int i) const { return sa.start(i * TPB) / BM; }  // clamped
+  __device__ __forceinline__ int col(int i) const { return sa.col(i); }  // clamped
   __device__ __forceinline__ void init(const PrefillParams& p, int qt, int rb, int re, int lane, int q_end) {
     t = qt;
     n_row = max(re - rb, 0);
-    sa.init(p, qt, false, rb, re, lane);
-    sa.trim(q_end);
+    sa.init(p, qt, false, rb, re, lane, q_end);
+    sa.check_diag();  // SA tiles in the diagonal-first order when the row allows it
     n_sa = sa.n_tiles;
     int distinct = 0, prev = -1;
     for (int i = 0; i < n_row; ++i) {
@@ -650,8 +678,7 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
     soft.init(p, t, rb, re, lane, q_end);
     n_tiles = soft.n_tiles;
   } else {
-    tiles.init(p, t, fa, rb, re, lane);
-    tiles.trim(q_end);
+    tiles.init(p, t, fa, rb, re, lane, q_end);
     n_tiles = tiles.n_tiles;
   }
   Loader ld;
@@ -659,8 +686,6 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   WaveAttn<D, BN> wa;
   const int wrow0 = q0 + wave * 32;
   wa.init(p.q, tok0, p.hq, head, wrow0, S, p.scale, lane);  // in flight with the first tile
-  // routed layers: the tiles are in increasing order, so a wave's are a prefix
-  const int n_mine = SOFT ? 0 : tiles.visible(wrow0, S);
   float r_fa = 1.0f;  // SOFT: the FA weight of this request and layer
   if constexpr (SOFT) r_fa = p.rsoft[static_cast<int64_t>(req) * p.n_layers + p.layer];
 
@@ -669,21 +694,27 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   // kst is the first key of tile n (looked up one step ahead, so no index
   // load waits behind the tile loads in flight).
   int kst = 0;
-  auto step = [&](int n, const lds_u8* kc, const lds_u8* vc, lds_u8* kn, lds_u8* vn) {
+  // routed: this wave computes tile n iff n < n_mine or n >= n_lo (set below)
+  int n_mine = 0, n_lo = 0;
+  auto step = [&](int n, const lds_u8* kc, const lds_u8* vc, lds_u8* kn, lds_u8* vn) __attribute__((always_inline)) {
     int kst_next = 0;
     if (n + 1 < n_tiles) {
       if constexpr (SOFT) {
         kst_next = soft.start(n + 1);
       } else {
-        // tiles of one mask block are contiguous: look the column up only at a block's first tile
-        kst_next = (n + 1) % TileList<BM, BN>::TPB != 0 ? kst + BN : tiles.start(n + 1);
+        kst_next = tiles.next_start(n, kst);
       }
       ld.issue(false, kst_next, kn);
       ld.issue(true, kst_next, vn);
     }
-    // SOFT tiles are not in key order: a wave computes the tiles that start
-    // at or before its last row
-    const bool mine = SOFT ? (wrow0 < S && kst <= wrow0 + 31) : n < n_mine;
+    // a wave computes the tiles that start at or before its last row (in the
+    // routed kernel's sorted orders these are a prefix of the tiles)
+    bool mine;
+    if constexpr (SOFT) {
+      mine = wrow0 < S && kst <= wrow0 + 31;
+    } else {
+      mine = n < n_mine || n >= n_lo;
+    }
     if (mine) {
       f32x4 sacc[2][2];
       uint32_t pk[WaveAttn<D, BN>::PK];
@@ -696,7 +727,7 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
     __syncthreads();
   };
   // tiles [n0, n1): tile n lives in buffer pair n & 1
-  auto run = [&](int n0, int n1) {
+  auto run = [&](int n0, int n1) __attribute__((always_inline)) {
     int n = n0;
     if (n < n1 && (n & 1)) step(n++, k1, v1, k0, v0);
     for (; n < n1; n += 2) {
@@ -705,14 +736,35 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
       step(n + 1, k1, v1, k0, v0);
     }
   };
-  if (n_tiles > 0) {
-    if constexpr (SOFT) {
+  if constexpr (SOFT) {
+    if (n_tiles > 0) {
       kst = soft.start(0);
-    } else {
-      kst = tiles.start(0);
+      ld.issue(false, kst, k0);
+      ld.issue(true, kst, v0);
     }
-    ld.issue(false, kst, k0);
-    ld.issue(true, kst, v0);
+  } else {
+    if (n_tiles > 0) {  // SA: the diagonal block's first tile, before the columns are known
+      kst = tiles.start(0);
+      ld.issue(false, kst, k0);
+      ld.issue(true, kst, v0);
+    }
+    if (tiles.check_diag()) {  // the row does not end with its diagonal block
+      n_tiles = tiles.n_tiles;
+      if (n_tiles > 0) {  // the earlier loads land first (in order); these replace them
+        kst = tiles.start(0);
+        ld.issue(false, kst, k0);
+        ld.issue(true, kst, v0);
+      }
+    }
+    if (tiles.diag_first) {  // the diagonal tiles up to the wave's last row, then every tile
+      n_mine = wrow0 < S ? min(tiles.n_diag, (wrow0 + 31 - t * BM) / BN + 1) : 0;
+      n_lo = wrow0 < S ? tiles.n_diag : n_tiles;
+    } else {  // sorted: a prefix
+      n_mine = tiles.visible_prefix(wrow0, S);
+      n_lo = n_tiles;
+    }
+  }
+  if (n_tiles > 0) {
     wait_vmem_all();
     __syncthreads();
   }

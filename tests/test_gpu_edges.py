@@ -191,3 +191,29 @@ def test_odd_gqa_groups(hq, hkv):
             ref = oracle.attention_decode(f32(qd[i:i + 1]), f32(kc[i:i + 1]), f32(vc[i:i + 1]), [n],
                                           route_rows[i][layer] == 1, m, B)
             assert_attn_close(f32(out[i:i + 1]), ref, f"decode group {hq // hkv} seq {i} layer {layer}")
+
+
+def test_sa_rows_without_their_diagonal_block():
+    """SA prefill on a hand-made mask whose odd rows leave out their diagonal
+    block: those rows are visited in their own order (the diagonal-first
+    order applies only to rows that end with the diagonal block), even rows
+    start with it; every row against the oracle."""
+    S, hq, hkv, d, B = 1000, 4, 2, 64, 64
+    nb = -(-S // B)
+    m = np.zeros((nb, nb), dtype=np.uint8)
+    for i in range(nb):
+        m[i, 0] = 1
+        for j in range(1, i):
+            if j % 3 == 1:
+                m[i, j] = 1
+        if i % 2 == 0:
+            m[i, i] = 1
+    rp_h, ci_h = oracle.mask_to_csr(m)
+    say("SA prefill, rows without their diagonal block")
+    q, k, v, cu, sa, _, _, route = run_prefill_case([S], hq, hkv, d, B, 1, 1, [[0]], 1400)
+    rp = torch.tensor(rp_h, dtype=torch.int32, device=DEV)
+    ci = torch.tensor(ci_h, dtype=torch.int32, device=DEV)
+    out = flux.attn_prefill(q, k, v, cu, S, route, 0, rp, ci, sa)
+    torch.cuda.synchronize()
+    ref = oracle.attention_prefill(f32(q), f32(k), f32(v), False, m, B)
+    assert_attn_close(f32(out), ref, "SA, rows without their diagonal block")
