@@ -19,11 +19,19 @@ layers with distinct caches (72 GiB), a seeded route with exactly 18 SA layers;
 one step = 36 flux_attn_decode calls; tok/s = 16 / step time.
 
 Roofline: the dominant kernel is the prefill kernel; achieved = algorithmic
-(computed-block) flops of its launches / their summed duration, timed with HIP
-events on the launch stream.  Computed-block flops per layer =
-active 128x128 blocks * 4 * 128^2 * head_dim * hq (FA: all 32896 causal
-blocks; SA: 4216 blocks).  Decode bytes per step = K+V bytes the layers must
-read (FA: all 32768 keys, SA: 17 blocks of 128 keys).
+flops of its launches / their summed duration, timed with HIP events on the
+launch stream.  Flops per layer = (32-row wave, 32-key tile) pairs the kernel
+executes * 4 * 32 * 32 * head_dim * hq (a wave skips the key tiles past its
+last row, so a diagonal 128-block runs 10 of its 16 pairs); the active
+128x128 block count and the attending (query, key) pair count are reported
+beside it.  Decode bytes per step = K+V bytes the layers must read (FA: all
+32768 keys, SA: 17 blocks of 128 keys).
+
+Also timed, each in its own JSON object: the 131072-token 36-layer routed
+prefill, an 8-prompt packed prefill + decode (varlen8), head- vs layer-level
+routing, the soft-routed pass, the content-aware mask, compact SA caches, a
+tiny 2-layer stack part by part, the router alone, and the float64 oracle on
+the host cores (cpu_baseline).
 """
 
 import argparse
