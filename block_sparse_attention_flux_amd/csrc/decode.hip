@@ -8,9 +8,10 @@
 //
 //   work list = every (sequence, kv head) unit visits U keys (all N keys for
 //               FA, the mask row's blocks for SA); the units are cut into
-//               work items of about the same number of keys (1024 items for
-//               equal units, at least 256 keys each), so a long FA sequence
-//               beside short SA ones gets proportionally more items.  Each
+//               work items of about the same number of keys (as many items
+//               as the GPU holds split workgroups at once, at least 256 keys
+//               each), so a long FA sequence beside short SA ones gets
+//               proportionally more items.  Each
 //               workgroup plans the whole call itself (every unit's U, its
 //               share of the items, one block-wide prefix sum) and takes item
 //               blockIdx.x: the plan costs no extra launch;
@@ -77,14 +78,15 @@ static_assert(kPlanPerThread * kWaves * 64 == kDecodePlanUnits, "plan units must
 
 // Balanced plan, computed by every workgroup for the whole call.  Thread t
 // owns units [4t, 4t + 4) (unit u = b * hkv + g).  With `total` the keys of
-// all units and T = ceil(total / (1024 - n_units / 2)), unit u gets
+// all units, `target` the split workgroups the GPU holds at once and
+// T = ceil(total / (target - n_units / 2)), unit u gets
 //   s_u = max(1, min(ceil(U_u / T), floor(U_u / 256)))
 // items of about U_u / s_u <= T keys each (chunk aligned), in consecutive
 // slots after those of the units before it: every item holds about the same
-// number of keys, and a call of equal units has exactly 1024 items (two
-// rounds of the 512 workgroups the GPU holds at once).  Returns false when no
-// unit owns item blockIdx.x.  Workgroup 0 also records (first slot, items)
-// per unit for the combine kernel.
+// number of keys, and a call of equal units has exactly `target` items (one
+// round of the resident workgroups).  Returns false when no unit owns item
+// blockIdx.x.  Workgroup 0 also records (first slot, items) per unit for the
+// combine kernel.
 __device__ bool plan_balanced(const DecodeParams& p, int tid, int lane, int wave, double* tot_sh,
                               int* cnt_sh, int* item_sh, DecodeItem& it) {
   constexpr int K = kPlanPerThread;
@@ -179,9 +181,10 @@ __device__ bool plan_balanced(const DecodeParams& p, int tid, int lane, int wave
     return first;
   };
   // Rounding each unit up adds half an item per unit on average, so the first
-  // pass aims at 1024 - n_units / 2 items.  If the count passes the grid
-  // (min(1024, n_units + max keys / 256) workgroups), the second pass aims
-  // at 1024 - n_units: sum ceil(U_u / T) <= total / T + n_units <= 1024.
+  // pass aims at target - n_units / 2 items.  If the count passes the grid
+  // (p.slots workgroups, at least min(target, n_units + max keys / 256)), the
+  // second pass aims at target - n_units: sum ceil(U_u / T) <= total / T +
+  // n_units <= target.
   int all = 0;
   int first = prefix(shares(max(p.target - n_units / 2, 1)), cnt_sh, all);
   if (all > p.slots) first = prefix(shares(max(p.target - n_units, 1)), cnt_sh + kWaves, all);
