@@ -440,12 +440,23 @@ struct WaveAttn {
       }
     }
     constexpr int RPI = 64 / CH;  // rows per 16-byte-per-lane instruction
+    constexpr int NI = 32 / RPI, NB = NI > 4 ? 4 : NI;
+    // LDS reads in batches of NB, each batch in flight together (read inside
+    // the row check, every read waited for its own round trip)
 #pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int r = RPI * i + lane / CH, chunk = lane % CH;
-      const u32x4 v = *reinterpret_cast<const lds_u32x4*>(stage + r * (D * 2) + ((chunk ^ swz(r)) * 16));
-      if (wrow0 + r < S)  // streaming store: this kernel never reads O back
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + (static_cast<size_t>(tok0 + wrow0 + r) * hq + head) * D + chunk * 8));
+    for (int i0 = 0; i0 < NI; i0 += NB) {
+      u32x4 v[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int r = RPI * (i0 + i) + lane / CH, chunk = lane % CH;
+        v[i] = *reinterpret_cast<const lds_u32x4*>(stage + r * (D * 2) + ((chunk ^ swz(r)) * 16));
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int r = RPI * (i0 + i) + lane / CH, chunk = lane % CH;
+        if (wrow0 + r < S)  // streaming store: this kernel never reads O back
+          __builtin_nontemporal_store(v[i], reinterpret_cast<u32x4*>(out + (static_cast<size_t>(tok0 + wrow0 + r) * hq + head) * D + chunk * 8));
+      }
     }
   }
 };
