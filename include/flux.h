@@ -221,9 +221,11 @@ flux_status flux_attn_prefill_heads(const uint16_t* q, const uint16_t* k, const 
  *   out = r * FA(q, k, v) + (1 - r) * SA(q, k, v),  r = r_soft[req][layer],
  * the convex combination of the two branches that the router's continuous
  * weight forms during training (technical summary, section 2, differentiable
- * soft routing).  One pass: every key tile up to the diagonal feeds the FA
- * state, and the tiles of the mask's blocks (a subset) also feed a second,
- * SA state from the same scores and the same K/V tiles.  Forward only.
+ * soft routing).  One pass with one softmax state: the tiles of the mask's
+ * blocks come first, then (1 - r) times their normalised result is parked
+ * in `out` (rounded to bf16 once), the same state runs on over FA's other
+ * causal tiles (the SA blocks are a subset of FA's), and r times the FA
+ * result plus the parked part is written.  Forward only.
  * r_soft [device] fp32 [n_req][n_layers] (the caller's weights, e.g. a
  * Gumbel-softmax sample or sigmoid(z); any value is combined as given).
  * Everything else as flux_attn_prefill (no route: both branches are formed).
@@ -245,9 +247,10 @@ size_t flux_attn_decode_workspace_size(int32_t n_seq, int32_t hq, int32_t hkv,
  * flux_attn_decode -- one decode step of one layer, split-KV over a work
  * list: every (sequence, kv head) visits U keys (FA: its N keys; SA: its
  * mask row's blocks), and the keys of all of them are cut into work items
- * of about the same size (at most 1024 items per call, at least 256 keys
- * each; a call with more than 1024 (sequence, kv head) pairs takes one item
- * per pair), so a long FA sequence beside short SA sequences is split
+ * of about the same size (about as many items as the GPU holds decode
+ * workgroups at once, at most 1024, at least 256 keys each; a call with more
+ * than 1024 (sequence, kv head) pairs takes one item per pair), so a long FA
+ * sequence beside short SA sequences is split
  * finer than they are.  The plan is made on the device from the lengths and
  * routes of the call; the partial results of a pair's items are merged by
  * the log-sum-exp rule.
