@@ -154,10 +154,12 @@ def main():
     def mask_call():
         check(F.flux_build_block_mask(S, sa.c(), None, P(row_ptr), P(col_idx), cstream), "mask")
 
+    pws = flux.prefill_workspace(dev)  # the balancing workspace of this stream (left zero by every call)
+
     def prefill_call(layer):
         check(F.flux_attn_prefill(P(q), P(k), P(v), P(out[layer]), P(cu), 1, S, hq, hkv, d,
                                   1.0 / math.sqrt(d), P(route), wl.n_layers, layer, P(row_ptr),
-                                  P(col_idx), nb, sa.c(), cstream), "prefill")
+                                  P(col_idx), nb, sa.c(), P(pws), pws.numel() * 4, cstream), "prefill")
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
@@ -319,6 +321,7 @@ def run_tiny(flux, syn, dev, stream, log, reps=200):
     rp = torch.empty(nb + 1, dtype=torch.int32, device=dev)
     ci = torch.empty(flux.mask_nnz(S, sa), dtype=torch.int32, device=dev)
     ws = flux.decode_workspace(1, wl.hq, wl.hkv, wl.head_dim, S, dev)
+    pws = flux.prefill_workspace(dev)
     outs = [torch.empty_like(q) for _ in range(2)]
     douts = [torch.empty_like(qd) for _ in range(2)]
     L, F = flux._lib, flux._LIB
@@ -333,7 +336,8 @@ def run_tiny(flux, syn, dev, stream, log, reps=200):
         ("mask", lambda: F.flux_build_block_mask(S, sa.c(), None, P(rp), P(ci), cs)),
     ] + [(f"prefill_{n}", (lambda layer: lambda: F.flux_attn_prefill(
             P(q), P(k), P(v), P(outs[layer]), P(cu), 1, S, wl.hq, wl.hkv, wl.head_dim,
-            1.0 / math.sqrt(wl.head_dim), P(route), 2, layer, P(rp), P(ci), nb, sa.c(), cs))(layer))
+            1.0 / math.sqrt(wl.head_dim), P(route), 2, layer, P(rp), P(ci), nb, sa.c(), P(pws),
+            pws.numel() * 4, cs))(layer))
          for layer, n in ((0, "fa"), (1, "sa"))
     ] + [(f"decode_{n}", (lambda layer: lambda: F.flux_attn_decode(
             P(qd), P(kc), P(vc), P(douts[layer]), P(sl), 1, S, wl.hq, wl.hkv, wl.head_dim,

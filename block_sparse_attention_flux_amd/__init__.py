@@ -25,7 +25,7 @@ _LIB = _lib.load()
 __all__ = [
     "SAParams", "FluxError", "route", "route_workspace_size", "mask_blocks", "mask_nnz", "build_block_mask",
     "build_block_mask_dynamic",
-    "attn_prefill", "attn_prefill_soft", "decode_workspace_size", "decode_workspace", "attn_decode",
+    "attn_prefill", "attn_prefill_soft", "prefill_workspace", "decode_workspace_size", "decode_workspace", "attn_decode",
     "attn_decode_append", "attn_decode_noalloc", "status_str",
     "kv_rows", "kv_cache", "kv_store_prefill", "kv_append", "attn_decode_sa_compact",
     "probe_mfma", "probe_read",
@@ -173,10 +173,44 @@ def _route_fn(route, hkv, layer_fn, head_fn, what):
     raise ValueError(f"{what}: route must be [n][n_layers] or [n][n_layers][hkv]")
 
 
+_PREFILL_WS = {}
+
+
+def prefill_workspace(device="cuda"):
+    """The zero-filled FLUX_PREFILL_WORKSPACE_BYTES workspace of the device's
+    current stream: made once per (device, stream) and reused, since every
+    prefill call leaves it zero again.  Calls on one stream run one after
+    another, so they never use it at the same time."""
+    device = torch.device(device)
+    if device.index is None:
+        device = torch.device(device.type, torch.cuda.current_device())
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _PREFILL_WS.get(key)
+    if ws is None:
+        ws = torch.zeros(_lib.FLUX_PREFILL_WORKSPACE_BYTES // 4, dtype=torch.int32, device=device)
+        _PREFILL_WS[key] = ws
+    return ws
+
+
+def _prefill_ws_args(workspace, device):
+    """(pointer, bytes) for workspace="auto" (the stream's own), None (the
+    fixed work order) or a caller's zero-filled int32 tensor."""
+    if workspace is None:
+        return None, 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a tensor')
+        workspace = prefill_workspace(device)
+    return _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size()
+
+
 def attn_prefill(q, k, v, cu_seqlens, max_seqlen, route, layer, row_ptr, col_idx, sa,
-                 out=None, softmax_scale=None):
+                 out=None, softmax_scale=None, workspace="auto"):
     """One routed attention layer over packed prompts (flux_attn_prefill, or
-    flux_attn_prefill_heads for a per-kv-head route [n_req][n_layers][hkv])."""
+    flux_attn_prefill_heads for a per-kv-head route [n_req][n_layers][hkv]).
+    workspace: "auto" (the stream's balancing workspace), None (the fixed
+    work order) or a zero-filled int32 tensor of FLUX_PREFILL_WORKSPACE_BYTES;
+    per-kv-head routes take none."""
     T, hq, d = q.shape
     hkv = k.shape[1]
     if k.shape != (T, hkv, d) or v.shape != (T, hkv, d):
@@ -186,21 +220,24 @@ def attn_prefill(q, k, v, cu_seqlens, max_seqlen, route, layer, row_ptr, col_idx
         out = torch.empty_like(q)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
-    code = fn(
+    args = [
         _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"),
         _ptr(out, torch.bfloat16, "out"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
         cu_seqlens.numel() - 1, int(max_seqlen), hq, hkv, d, float(softmax_scale),
         _ptr(route, torch.uint8, "route"), route.shape[1], int(layer),
         _ptr(row_ptr, torch.int32, "row_ptr"), _ptr(col_idx, torch.int32, "col_idx"),
-        row_ptr.numel() - 1, sa.c(), _stream(q.device))
+        row_ptr.numel() - 1, sa.c()]
+    if fn is _LIB.flux_attn_prefill:
+        args += list(_prefill_ws_args(workspace, q.device))
+    code = fn(*args, _stream(q.device))
     _check(code, "flux_attn_prefill")
     return out
 
 
 def attn_prefill_soft(q, k, v, cu_seqlens, max_seqlen, r_soft, layer, row_ptr, col_idx, sa,
-                      out=None, softmax_scale=None):
+                      out=None, softmax_scale=None, workspace="auto"):
     """Soft-routed forward r FA + (1 - r) SA of one layer (flux_attn_prefill_soft);
-    r_soft float32 [n_req][n_layers]."""
+    r_soft float32 [n_req][n_layers]; workspace as for attn_prefill."""
     T, hq, d = q.shape
     hkv = k.shape[1]
     if k.shape != (T, hkv, d) or v.shape != (T, hkv, d):
@@ -215,7 +252,7 @@ def attn_prefill_soft(q, k, v, cu_seqlens, max_seqlen, r_soft, layer, row_ptr, c
         cu_seqlens.numel() - 1, int(max_seqlen), hq, hkv, d, float(softmax_scale),
         _ptr(r_soft, torch.float32, "r_soft"), r_soft.shape[1], int(layer),
         _ptr(row_ptr, torch.int32, "row_ptr"), _ptr(col_idx, torch.int32, "col_idx"),
-        row_ptr.numel() - 1, sa.c(), _stream(q.device))
+        row_ptr.numel() - 1, sa.c(), *_prefill_ws_args(workspace, q.device), _stream(q.device))
     _check(code, "flux_attn_prefill_soft")
     return out
 

@@ -18,6 +18,7 @@ FLUX_ERR_HIP = -4
 FLUX_F32 = 0
 FLUX_BF16 = 1
 FLUX_DECODE_SCRATCH_BYTES = 9 << 20
+FLUX_PREFILL_WORKSPACE_BYTES = 64
 
 
 class SAParamsC(ctypes.Structure):
@@ -45,15 +46,16 @@ SIGNATURES = [
     ("flux_dynamic_mask_workspace_size", _S, [_I, _I, _I, _I, _I]),
     ("flux_build_block_mask_dynamic", _I, [_P, _P, _I, _I, _I, _I, _F, DynParamsC, _P, _P,
                                            ctypes.c_int64, _P, _S, _P]),
+    ("flux_attn_prefill_workspace_size", _S, []),
     ("flux_attn_prefill", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P, _P,
-                               _I, SAParamsC, _P]),
+                               _I, SAParamsC, _P, _S, _P]),
     ("flux_attn_decode_workspace_size", _S, [_I, _I, _I, _I, _I]),
     ("flux_attn_decode", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P, _P, _I,
                               SAParamsC, _P, _S, _P]),
     ("flux_attn_prefill_heads", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P,
                                      _P, _I, SAParamsC, _P]),
     ("flux_attn_prefill_soft", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P,
-                                    _P, _I, SAParamsC, _P]),
+                                    _P, _I, SAParamsC, _P, _S, _P]),
     ("flux_attn_decode_append", _I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I,
                                      _P, _P, _I, SAParamsC, _P, _S, _P]),
     ("flux_attn_decode_noalloc", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _P, _P,

@@ -50,9 +50,13 @@ flux_status attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          int32_t hkv, int32_t head_dim, float softmax_scale, const uint8_t* route,
                          int32_t n_layers, int32_t layer, const int32_t* mask_row_ptr,
                          const int32_t* mask_col_idx, int32_t mask_blocks, flux_sa_params p,
-                         int32_t route_heads, const float* rsoft, void* stream) {
+                         int32_t route_heads, const float* rsoft, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || cu_seqlens == nullptr)
     return FLUX_ERR_INVALID_ARG;
+  if (workspace != nullptr &&
+      (workspace_bytes < FLUX_PREFILL_WORKSPACE_BYTES || reinterpret_cast<uintptr_t>(workspace) % 16 != 0))
+    return FLUX_ERR_WORKSPACE;
   if (out == q || out == k || out == v) return FLUX_ERR_INVALID_ARG;
   if (n_req < 1 || max_seqlen < 1) return FLUX_ERR_INVALID_ARG;
   const flux_status st = check_attn_common(hq, hkv, head_dim, softmax_scale, route, n_layers, layer,
@@ -73,6 +77,13 @@ flux_status attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
   pp.scale = softmax_scale;
   pp.route_heads = route_heads;
   pp.rsoft = rsoft;
+  // balanced order: one prompt with one route decision per layer, whole XCD
+  // shares (items % 8 == 0), at least one full round of the GPU's
+  // workgroups (768) and room in a 32-bit grid for the extra items / 8
+  const int64_t items = n_qt * hq * n_req;
+  if (workspace != nullptr && n_req == 1 && route_heads == 1 && items % 8 == 0 && items >= 768 &&
+      items + items / 8 <= INT32_MAX)
+    pp.wq = static_cast<int32_t*>(workspace);
   return from_hip(flux::launch_prefill(pp, static_cast<hipStream_t>(stream)));
 }
 
@@ -264,11 +275,13 @@ flux_status flux_attn_prefill(const uint16_t* q, const uint16_t* k, const uint16
                               float softmax_scale, const uint8_t* route, int32_t n_layers,
                               int32_t layer, const int32_t* mask_row_ptr,
                               const int32_t* mask_col_idx, int32_t mask_blocks, flux_sa_params p,
-                              void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream) {
   return attn_prefill(q, k, v, out, cu_seqlens, n_req, max_seqlen, hq, hkv, head_dim,
                       softmax_scale, route, n_layers, layer, mask_row_ptr, mask_col_idx,
-                      mask_blocks, p, 1, nullptr, stream);
+                      mask_blocks, p, 1, nullptr, workspace, workspace_bytes, stream);
 }
+
+size_t flux_attn_prefill_workspace_size(void) { return FLUX_PREFILL_WORKSPACE_BYTES; }
 
 flux_status flux_attn_prefill_heads(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                     uint16_t* out, const int32_t* cu_seqlens, int32_t n_req,
@@ -279,7 +292,7 @@ flux_status flux_attn_prefill_heads(const uint16_t* q, const uint16_t* k, const 
                                     flux_sa_params p, void* stream) {
   return attn_prefill(q, k, v, out, cu_seqlens, n_req, max_seqlen, hq, hkv, head_dim,
                       softmax_scale, route, n_layers, layer, mask_row_ptr, mask_col_idx,
-                      mask_blocks, p, hkv, nullptr, stream);
+                      mask_blocks, p, hkv, nullptr, nullptr, 0, stream);
 }
 
 flux_status flux_attn_prefill_soft(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -288,12 +301,14 @@ flux_status flux_attn_prefill_soft(const uint16_t* q, const uint16_t* k, const u
                                    float softmax_scale, const float* r_soft, int32_t n_layers,
                                    int32_t layer, const int32_t* mask_row_ptr,
                                    const int32_t* mask_col_idx, int32_t mask_blocks,
-                                   flux_sa_params p, void* stream) {
+                                   flux_sa_params p, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
   if (r_soft == nullptr) return FLUX_ERR_INVALID_ARG;
   // the weights take the route's place in the shared checks (the route itself is not read)
   return attn_prefill(q, k, v, out, cu_seqlens, n_req, max_seqlen, hq, hkv, head_dim,
                       softmax_scale, reinterpret_cast<const uint8_t*>(r_soft), n_layers, layer,
-                      mask_row_ptr, mask_col_idx, mask_blocks, p, 1, r_soft, stream);
+                      mask_row_ptr, mask_col_idx, mask_blocks, p, 1, r_soft, workspace,
+                      workspace_bytes, stream);
 }
 
 size_t flux_attn_decode_workspace_size(int32_t n_seq, int32_t hq, int32_t hkv, int32_t head_dim,

@@ -52,7 +52,9 @@
 // exactly 1, so each row depends on its own data only.
 //
 // Workgroups are ordered so that each XCD (own L2) works through whole KV
-// head groups, heaviest causal rows first.
+// head groups, heaviest causal rows first.  With a workspace, the last 40 % of
+// each XCD's list of an FA layer over one prompt is handed out at run time,
+// so XCDs that run faster than the others take over part of their tails.
 #include "flux_device.h"
 #include "flux_internal.h"
 
@@ -605,9 +607,11 @@ struct SoftOrder {
 // one decision per kv head the XCD-major order would leave the XCDs that drew
 // FA groups running long after the others, so there each XCD's share cycles
 // through all kv groups instead (heaviest query blocks still first).
-__device__ __forceinline__ void decode_work(int n_slots, int n_req, int n_qt, int hkv, bool by_head,
+//
+// bid is the item's place in that order and G the number of items (equal to
+// the grid, except in the balanced order below).
+__device__ __forceinline__ void decode_work(int bid, int G, int n_slots, int n_req, int n_qt, int hkv, bool by_head,
                                             int& slot, int& req, int& t, int& g) {
-  const int G = gridDim.x, bid = blockIdx.x;
   int w;
   if (by_head && G % (8 * hkv) == 0) {
     const int i = bid / 8;
@@ -628,6 +632,51 @@ __device__ __forceinline__ void decode_work(int n_slots, int n_req, int n_qt, in
   req = w % n_req;
   g = w / n_req;
 }
+
+// Balanced order (p.wq: a caller's zeroed workspace; the host sets it only
+// for one prompt, one route decision per layer and items % 8 == 0).  The
+// eight XCDs finish equal static shares of an FA layer up to ~10 % apart,
+// and which XCD is slow changes from run to run, so only the first 60 % of
+// each XCD's list is static.  The rest of XCD x's list is queue x: a tail
+// workgroup of an FA layer takes the next item of the queue of the XCD it
+// runs on (hardware register XCC_ID), or, when that is empty, of the first
+// other queue with items left.  The grid has items / 8 more workgroups than
+// items; every tail workgroup either takes one item or finds all queues
+// empty and ends, and since there are at least as many tail workgroups as
+// tail items, every item is taken exactly once.  wq[0..7] count the items
+// taken from each queue, wq[8] the tail workgroups done; the last one sets
+// all nine back to zero, so the workspace is zero again when the launch
+// completes.  SA layers (short, equal items whose K/V sits in their own
+// XCD's L2) keep the fixed order: their tail workgroups take item blockIdx,
+// and the extra ones end.
+struct Balance {
+  static constexpr int kTailPct = 40;
+  int items, per, stat;  // items, items per XCD, static items per XCD
+  __device__ __forceinline__ void init(int n_items) {
+    items = n_items;
+    per = n_items / 8;
+    stat = per - static_cast<int>(static_cast<int64_t>(per) * kTailPct / 100);
+  }
+  __device__ __forceinline__ bool tail_wg(const PrefillParams& p) const {
+    return p.wq != nullptr && static_cast<int>(gridDim.x) > items && static_cast<int>(blockIdx.x) >= 8 * stat;
+  }
+  // item of this tail workgroup in the XCD-major order, or -1 (thread 0)
+  __device__ __forceinline__ int take(const PrefillParams& p) const {
+    const int x = __builtin_amdgcn_s_getreg((31 << 11) | 20) & 7;  // hwreg(HW_REG_XCC_ID)
+    const int tail = per - stat;
+    for (int k = 0; k < 8; ++k) {
+      const int y = (x + k) & 7;
+      const int i = atomicAdd(&p.wq[y], 1);
+      if (i < tail) return (stat + i) * 8 + y;
+    }
+    return -1;
+  }
+  __device__ __forceinline__ void done(const PrefillParams& p) const {  // thread 0 of a queue user
+    const int n_tail_wg = static_cast<int>(gridDim.x) - 8 * stat;
+    if (atomicAdd(&p.wq[8], 1) == n_tail_wg - 1)
+      for (int k = 0; k < 9; ++k) atomicExch(&p.wq[k], 0);
+  }
+};
 
 // SOFT: the soft-routed forward, O = r FA + (1 - r) SA with r per (request,
 // layer), with one softmax state (SoftOrder): the SA tiles come first; after
@@ -657,7 +706,28 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   const int group = p.hq / p.hkv;
   const int n_qt = (p.max_seqlen + BM - 1) / BM;
   int hi, req, t, g;
-  decode_work(group, p.n_req, n_qt, p.hkv, p.route_heads > 1, hi, req, t, g);
+  Balance bal;
+  bal.init(n_qt * p.hq * p.n_req);
+  int bid = blockIdx.x;
+  bool queued = false;  // this workgroup took its item from the queues
+  if (bal.tail_wg(p)) {
+    __shared__ int item_sh, queued_sh;
+    if (tid == 0) {
+      // the one prompt's route decides (the soft pass does FA's work)
+      const bool fa = SOFT || p.route[route_index(0, p.n_layers, p.layer, 1, 0)] != 0;
+      item_sh = fa ? bal.take(p) : (bid < bal.items ? bid : -1);
+      queued_sh = fa;
+    }
+    __syncthreads();
+    bid = __builtin_amdgcn_readfirstlane(item_sh);
+    queued = __builtin_amdgcn_readfirstlane(queued_sh) != 0;
+    if (bid < 0) {
+      if (queued && tid == 0) bal.done(p);
+      return;
+    }
+  }
+  decode_work(bid, p.wq != nullptr ? bal.items : static_cast<int>(gridDim.x), group, p.n_req, n_qt, p.hkv,
+              p.route_heads > 1, hi, req, t, g);
   const int head = g * group + hi;
 
   // Sequence bounds, the mask row's CSR bounds and the route byte: one
@@ -678,7 +748,10 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   const int rb = __builtin_amdgcn_readlane(gv, 2), re = __builtin_amdgcn_readlane(gv, 3);
   const int rbyte = __builtin_amdgcn_readlane(gv, 4);
   const int q0 = t * BM;
-  if (q0 >= S) return;
+  if (q0 >= S) {
+    if (queued && tid == 0) bal.done(p);
+    return;
+  }
   const bool fa = SOFT || rbyte != 0;
   const int q_end = min(q0 + BM, S);
 
@@ -798,12 +871,14 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   } else {
     wa.store(p.out, tok0, p.hq, head, S, stage, lane);
   }
+  if (queued && tid == 0) bal.done(p);
 }
 
 template <int D, int BM>
 hipError_t launch_typed(const PrefillParams& p, hipStream_t s) {
   const int n_qt = (p.max_seqlen + BM - 1) / BM;
-  const int64_t grid = static_cast<int64_t>(n_qt) * p.hq * p.n_req;
+  const int64_t items = static_cast<int64_t>(n_qt) * p.hq * p.n_req;
+  const int64_t grid = p.wq != nullptr ? items + items / 8 : items;
   // 64-row blocks: 2-wave workgroups whose tiles hold LDS for 2 waves per SIMD
   constexpr int occ = BM == 128 ? kOcc : 2;
   if (p.rsoft != nullptr)

@@ -188,16 +188,33 @@ flux_status flux_build_block_mask_dynamic(const uint16_t* q, const uint16_t* k, 
  *             be increasing within a row (columns past a row's diagonal are
  *             clamped to it).  Every workgroup reads its row's bounds; only SA
  *             layers read the columns.
+ * workspace   [device] NULL, or FLUX_PREFILL_WORKSPACE_BYTES (16-byte
+ *             aligned, owned by the caller) that are all zero before the call;
+ *             the call leaves them all zero again when it completes.  For an
+ *             FA layer over one prompt, the last part of every XCD's share of
+ *             the work is then handed out at run time, so XCDs that run
+ *             faster than the others take over some of their work (other
+ *             calls keep the fixed order).  Results are bitwise those without
+ *             a workspace: only which workgroup computes a query block
+ *             changes.  Calls that run at the same time need different
+ *             workspaces.  A size below FLUX_PREFILL_WORKSPACE_BYTES or a
+ *             misaligned pointer is FLUX_ERR_WORKSPACE.
  * Supported: head_dim in {64, 128}, block_size in {64, 128}, hq % hkv == 0,
  *            hq / hkv <= 16.  out may not alias q, k or v.
  */
+#define FLUX_PREFILL_WORKSPACE_BYTES ((size_t)64)
+
+/* FLUX_PREFILL_WORKSPACE_BYTES [host]. */
+size_t flux_attn_prefill_workspace_size(void);
+
 flux_status flux_attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               uint16_t* out, const int32_t* cu_seqlens, int32_t n_req,
                               int32_t max_seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
                               float softmax_scale, const uint8_t* route, int32_t n_layers,
                               int32_t layer, const int32_t* mask_row_ptr,
                               const int32_t* mask_col_idx, int32_t mask_blocks,
-                              flux_sa_params p, void* stream);
+                              flux_sa_params p, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * flux_attn_prefill_heads -- flux_attn_prefill with one route decision per
@@ -206,7 +223,8 @@ flux_status flux_attn_prefill(const uint16_t* q, const uint16_t* k, const uint16
  * granularity the pages argue against on GPUs (load imbalance and
  * synchronisation long tails between heads; technical summary, sections 1
  * and 2); it is provided to measure that claim.  Everything else as
- * flux_attn_prefill.
+ * flux_attn_prefill, without the workspace (a fixed order that deals every
+ * kv group to every XCD).
  */
 flux_status flux_attn_prefill_heads(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                     uint16_t* out, const int32_t* cu_seqlens, int32_t n_req,
@@ -228,7 +246,8 @@ flux_status flux_attn_prefill_heads(const uint16_t* q, const uint16_t* k, const 
  * result plus the parked part is written.  Forward only.
  * r_soft [device] fp32 [n_req][n_layers] (the caller's weights, e.g. a
  * Gumbel-softmax sample or sigmoid(z); any value is combined as given).
- * Everything else as flux_attn_prefill (no route: both branches are formed).
+ * Everything else, the workspace included, as flux_attn_prefill (no route:
+ * both branches are formed; the pass balances like an FA layer).
  */
 flux_status flux_attn_prefill_soft(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    uint16_t* out, const int32_t* cu_seqlens, int32_t n_req,
@@ -236,7 +255,8 @@ flux_status flux_attn_prefill_soft(const uint16_t* q, const uint16_t* k, const u
                                    float softmax_scale, const float* r_soft, int32_t n_layers,
                                    int32_t layer, const int32_t* mask_row_ptr,
                                    const int32_t* mask_col_idx, int32_t mask_blocks,
-                                   flux_sa_params p, void* stream);
+                                   flux_sa_params p, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /* Workspace bytes flux_attn_decode needs for these sizes [host] (0 on invalid
  * input). */

@@ -31,7 +31,7 @@ def declared_symbols(header=HEADER):
 
 def test_exports_every_declared_symbol():
     syms = declared_symbols()
-    assert len(syms) == 20, syms
+    assert len(syms) == 21, syms
     raw = ctypes.CDLL(LIB)
     for s in syms:
         assert hasattr(raw, s), s
@@ -103,14 +103,14 @@ def test_route_validation():
 
 PREFILL_OK = dict(q=FAKE, k=FAKE, v=ctypes.c_void_p(0x2000), out=ctypes.c_void_p(0x3000), cu=FAKE,
                   n_req=1, max_seqlen=512, hq=4, hkv=2, d=64, scale=0.125, route=FAKE, L=2, layer=0,
-                  rp=FAKE, ci=FAKE, mb=8, sa=SA(64, 1, 2), stream=NULL)
+                  rp=FAKE, ci=FAKE, mb=8, sa=SA(64, 1, 2), ws=NULL, wsb=0, stream=NULL)
 
 
 def prefill(**kw):
     a = dict(PREFILL_OK, **kw)
     return lib.flux_attn_prefill(a["q"], a["k"], a["v"], a["out"], a["cu"], a["n_req"], a["max_seqlen"],
                                  a["hq"], a["hkv"], a["d"], a["scale"], a["route"], a["L"], a["layer"],
-                                 a["rp"], a["ci"], a["mb"], a["sa"], a["stream"])
+                                 a["rp"], a["ci"], a["mb"], a["sa"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -121,9 +121,18 @@ def prefill(**kw):
     (dict(sa=SA(64, 1, 0)), -1), (dict(sa=SA(64, -2, 1)), -1),
     (dict(mb=7), -1),                          # mask too small for max_seqlen
     (dict(d=96), -2), (dict(sa=SA(32, 1, 2)), -2), (dict(hq=34, hkv=2), -2),
+    (dict(ws=ctypes.c_void_p(0x4000), wsb=63), -3),                    # balancing workspace too small
+    (dict(ws=ctypes.c_void_p(0x4008), wsb=64), -3),                    # ... or not 16-byte aligned
+    (dict(ws=ctypes.c_void_p(0x4000), wsb=64, hq=5, hkv=2), -1),       # other checks still apply
 ])
 def test_prefill_validation(kw, code):
     assert prefill(**kw) == code
+
+
+def test_prefill_workspace_size():
+    """The balancing workspace is a fixed 64 bytes: 8 queue counters, one
+    count of finished workgroups, room to spare."""
+    assert lib.flux_attn_prefill_workspace_size() == _lib.FLUX_PREFILL_WORKSPACE_BYTES == 64
 
 
 def test_decode_workspace_size():
@@ -292,8 +301,14 @@ def test_head_route_and_soft_validation():
     OUT = ctypes.c_void_p(0x2000)
 
     def pre(fn, route=FAKE, hq=32, hkv=8, d=128, mb=256):
+        if fn is lib.flux_attn_prefill_soft:  # the soft pass takes the balancing workspace too
+            return fn(FAKE, FAKE, FAKE, OUT, FAKE, 1, 32768, hq, hkv, d, 0.088, route, 2, 0, FAKE, FAKE,
+                      mb, sa, NULL, 0, NULL)
         return fn(FAKE, FAKE, FAKE, OUT, FAKE, 1, 32768, hq, hkv, d, 0.088, route, 2, 0, FAKE, FAKE,
                   mb, sa, NULL)
+    assert lib.flux_attn_prefill_soft(FAKE, FAKE, FAKE, OUT, FAKE, 1, 32768, 32, 8, 128, 0.088, FAKE, 2, 0,
+                                      FAKE, FAKE, 256, sa, ctypes.c_void_p(0x4000), 32, NULL) \
+        == _lib.FLUX_ERR_WORKSPACE
     for fn in (lib.flux_attn_prefill_heads, lib.flux_attn_prefill_soft):
         assert pre(fn, route=NULL) == _lib.FLUX_ERR_INVALID_ARG   # route / r_soft missing
         assert pre(fn, hq=30) == _lib.FLUX_ERR_INVALID_ARG
