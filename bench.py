@@ -85,6 +85,8 @@ def parse():
     ap.add_argument("--no-long", action="store_true",
                     help="skip the 131072-token routed prefill and the varlen8 prefill + decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the decode steps with eager launches only (profiler runs, which serialise every launch)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 256 MiB device copy (counter calibration)")
     return ap.parse_args()
@@ -281,7 +283,7 @@ def main():
     # ------------------------------------------------------------ long workloads
     if not args.no_long:
         result["prefill131k"] = run_prefill_131k(flux, syn, dev, stream, log)
-        result["varlen8"] = run_varlen8(flux, syn, dev, stream, log)
+        result["varlen8"] = run_varlen8(flux, syn, dev, stream, log, graph=not args.no_graph)
 
     # ------------------------------------------------------------ oracle on the host
     if not args.no_cpu_baseline:
@@ -662,7 +664,7 @@ def run_prefill_131k(flux, syn, dev, stream, log):
     return res
 
 
-def run_varlen8(flux, syn, dev, stream, log):
+def run_varlen8(flux, syn, dev, stream, log, graph=True):
     """The varlen workload: 8 prompts (seeded lengths in [8192, 65536]), router
     4096 -> 256 -> 32 per request, all 32 layers of packed prefill routed per
     request (one q/k/v set shared by the layers), then 128 decode steps over 32
@@ -735,43 +737,47 @@ def run_varlen8(flux, syn, dev, stream, log):
             # the new token's K/V row is appended by the same launch
             flux.attn_decode_append(qd[t, layer], knew[t, layer], vnew[t, layer], kc[layer], vc[layer],
                                     seqlens, route, layer, rp, ci, sa, ws, out=dout)
+        if (t + 1) % 32 == 0:
+            log(f"varlen8 decode: {t + 1} eager steps launched")
     e1.record(stream)
     torch.cuda.synchronize()
     eager_ms = e0.elapsed_time(e1) / wl.decode_steps
+    dec_ms = eager_ms
 
     # The same 128 steps with one step captured as a HIP graph: the 32
     # decode-append launches on device-resident lengths, then the lengths'
     # increment, replayed once per step (every step reads the rows of its own
     # lengths, as above; its q and new rows are one fixed set).  The first
     # replay is checked bit for bit against the same step launched eagerly.
-    sl_dev = seq_t[0].clone()
-    douts = [torch.empty_like(dout) for _ in range(L)]
+    if graph:
+        sl_dev = seq_t[0].clone()
+        douts = [torch.empty_like(dout) for _ in range(L)]
 
-    def gstep():
-        for layer in range(L):
-            flux.attn_decode_append(qd[0, layer], knew[0, layer], vnew[0, layer], kc[layer], vc[layer],
-                                    sl_dev, route, layer, rp, ci, sa, ws, out=douts[layer])
-    gstep()
-    torch.cuda.synchronize()
-    eager_out = [o.clone() for o in douts]
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+        def gstep():
+            for layer in range(L):
+                flux.attn_decode_append(qd[0, layer], knew[0, layer], vnew[0, layer], kc[layer], vc[layer],
+                                        sl_dev, route, layer, rp, ci, sa, ws, out=douts[layer])
         gstep()
-        sl_dev.add_(1)
-    for o in douts:
-        o.zero_()
-    graph.replay()
-    torch.cuda.synchronize()
-    if not all(torch.equal(a, b) for a, b in zip(douts, eager_out)):
-        raise RuntimeError("varlen8 decode graph replay differs from the eager step")
-    sl_dev.copy_(seq_t[0])
-    e0.record(stream)
-    for _ in range(wl.decode_steps):
-        graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    dec_ms = e0.elapsed_time(e1) / wl.decode_steps
-    del graph
+        torch.cuda.synchronize()
+        eager_out = [o.clone() for o in douts]
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            gstep()
+            sl_dev.add_(1)
+        for o in douts:
+            o.zero_()
+        g_step.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(douts, eager_out)):
+            raise RuntimeError("varlen8 decode graph replay differs from the eager step")
+        sl_dev.copy_(seq_t[0])
+        e0.record(stream)
+        for _ in range(wl.decode_steps):
+            g_step.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dec_ms = e0.elapsed_time(e1) / wl.decode_steps
+        del g_step, douts, eager_out
     # bytes per step, averaged over the steps: every K/V row the step reads,
     # once (FA: the N cached keys; SA: the keys below N of its mask row's blocks)
     byts = decode_bytes_varlen(lens, r, wl, range(1, wl.decode_steps + 1)) / wl.decode_steps
@@ -787,13 +793,14 @@ def run_varlen8(flux, syn, dev, stream, log):
            "decode_eager_ms_per_step": round(eager_ms, 4),
            "decode_eager_frac_hbm": round(byts / (eager_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
            "decode_note": "each layer's step appends its new K/V row in the same launch (flux_attn_decode_append); "
-                          "decode_* = one step captured as a HIP graph (32 launches + the lengths' increment) replayed "
-                          "per step, the first replay bitwise equal to the eager step; decode_eager_* = every launch "
-                          "from Python; bytes are the K/V rows each step reads at its own cache length, averaged over "
-                          "the 128 steps"}
-    log(f"varlen8 decode: {dec_ms:.3f} ms/step as a graph replay, {eager_ms:.3f} eager "
+                          + ("decode_* = one step captured as a HIP graph (32 launches + the lengths' increment) "
+                             "replayed per step, the first replay bitwise equal to the eager step; decode_eager_* = "
+                             "every launch from Python" if graph else "eager launches only (--no-graph)")
+                          + "; bytes are the K/V rows each step reads at its own cache length, averaged over the "
+                            "128 steps"}
+    log(f"varlen8 decode: {dec_ms:.3f} ms/step ({'graph replay' if graph else 'eager'}), {eager_ms:.3f} eager "
         f"({res['decode_tok_s']:.0f} tok/s, {res['decode_gbs']:.0f} GB/s)")
-    del kc, vc, knew, vnew, qd, douts, eager_out
+    del kc, vc, knew, vnew, qd
     torch.cuda.empty_cache()
     return res
 
@@ -879,24 +886,26 @@ def run_decode(args, flux, syn, dev, stream, log):
     # The same step captured once in a HIP graph and replayed: the host's
     # launch gaps between the 72 kernels disappear.  Every checked replay must
     # reproduce the eager outputs bit for bit.
-    eager = [o.clone() for o in out]
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    for _ in range(2):
-        for o in out:
-            o.zero_()
-        graph.replay()
+    graph_ms = step_ms
+    if not args.no_graph:
+        eager = [o.clone() for o in out]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(2):
+            for o in out:
+                o.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(a, b) for a, b in zip(out, eager)):
+                raise RuntimeError("decode graph replay differs from the eager step")
+        e0.record(stream)
+        for _ in range(args.decode_steps):
+            graph.replay()
+        e1.record(stream)
         torch.cuda.synchronize()
-        if not all(torch.equal(a, b) for a, b in zip(out, eager)):
-            raise RuntimeError("decode graph replay differs from the eager step")
-    e0.record(stream)
-    for _ in range(args.decode_steps):
-        graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    graph_ms = e0.elapsed_time(e1) / args.decode_steps
-    del graph
+        graph_ms = e0.elapsed_time(e1) / args.decode_steps
+        del graph
 
     # The same step with the SA layers on compact caches (sink rows + a ring
     # of the window: 2176 rows per head instead of 32768); FA layers unchanged.
@@ -957,8 +966,9 @@ def run_decode(args, flux, syn, dev, stream, log):
         "workload": "Qwen3-4B-shaped decode, 16 seqs x 32768 ctx, 36 layers (18 FA / 18 SA seeded)",
         "value": round(n_seq / (graph_ms * 1e-3), 1), "unit": "tok/s",
         "ms_per_step": round(graph_ms, 4), "steps": args.decode_steps,
-        "launch": "the step's 72 launches captured once in a HIP graph and replayed (every checked replay "
-                  "bitwise equal to the eager step); eager_* = the same step launched from Python",
+        "launch": ("the step's 72 launches captured once in a HIP graph and replayed (every checked replay "
+                   "bitwise equal to the eager step); eager_* = the same step launched from Python")
+        if not args.no_graph else "eager launches only (--no-graph)",
         "eager_ms_per_step": round(step_ms, 4), "eager_tok_s": round(n_seq / (step_ms * 1e-3), 1),
         "pass_ms_per_step": [round(x, 4) for x in passes],
         "eager_gbs": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
