@@ -9,7 +9,8 @@ the queues, SA in the fixed order with the extra workgroups ending at once),
 a prompt shorter than max_seqlen (queue items past its end), the soft pass,
 64-wide heads and 64-row blocks, shapes below one round of workgroups and a
 packed batch (fixed order with a workspace passed), and the binding's
-per-stream workspace.  The oracle comparisons of every other prefill test run
+per-stream workspace, and a balanced launch replayed from a HIP graph.  The
+oracle comparisons of every other prefill test run
 with the workspace too (the binding's default)."""
 
 import pytest
@@ -144,3 +145,29 @@ def test_stream_workspace_is_reused_and_stays_zero():
         torch.cuda.synchronize()
         assert torch.equal(bits(again), bits(first))
         assert not ws.any()
+
+
+def test_balanced_prefill_under_graph_capture():
+    """A balanced FA launch captured in a HIP graph: every replay (with eager
+    work in between) reproduces the eager output and leaves the workspace
+    zero, since the kernel itself resets the counters."""
+    S, hq, hkv, d = 8192, 32, 8, 128
+    say("balanced prefill under graph capture")
+    q, k, v, cu, sa, rp, ci = inputs([S], hq, hkv, d, 128, 4, 8606)
+    route = torch.tensor([[1, 0]], dtype=torch.uint8, device=DEV)
+    ws = new_workspace()
+    out = torch.empty_like(q)
+    flux.attn_prefill(q, k, v, cu, S, route, 0, rp, ci, sa, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    eager = bits(out).clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        flux.attn_prefill(q, k, v, cu, S, route, 0, rp, ci, sa, out=out, workspace=ws)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.randn(1 << 20, device=DEV).sum()  # the program's own work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out), eager), f"replay {rep}"
+        assert not ws.any(), f"replay {rep}: workspace not zero"
