@@ -18,7 +18,7 @@ FLUX_ERR_HIP = -4
 FLUX_F32 = 0
 FLUX_BF16 = 1
 FLUX_DECODE_SCRATCH_BYTES = 9 << 20
-FLUX_PREFILL_WORKSPACE_BYTES = 64
+FLUX_PREFILL_WORKSPACE_BYTES = 1024
 
 
 class SAParamsC(ctypes.Structure):

@@ -77,12 +77,11 @@ flux_status attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
   pp.scale = softmax_scale;
   pp.route_heads = route_heads;
   pp.rsoft = rsoft;
-  // balanced order: one prompt with one route decision per layer, whole XCD
-  // shares (items % 8 == 0), at least one full round of the GPU's
-  // workgroups (768) and room in a 32-bit grid for the extra items / 8
+  // balanced order: one route decision per layer, whole XCD shares
+  // (items % 8 == 0), at least one full round of the GPU's workgroups (768)
+  // and room in a 32-bit grid for the extra items / 8
   const int64_t items = n_qt * hq * n_req;
-  if (workspace != nullptr && n_req == 1 && route_heads == 1 && items % 8 == 0 && items >= 768 &&
-      items + items / 8 <= INT32_MAX)
+  if (workspace != nullptr && route_heads == 1 && items % 8 == 0 && items >= 768 && items + items / 8 <= INT32_MAX)
     pp.wq = static_cast<int32_t*>(workspace);
   return from_hip(flux::launch_prefill(pp, static_cast<hipStream_t>(stream)));
 }

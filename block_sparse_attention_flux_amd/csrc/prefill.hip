@@ -52,9 +52,9 @@
 // exactly 1, so each row depends on its own data only.
 //
 // Workgroups are ordered so that each XCD (own L2) works through whole KV
-// head groups, heaviest causal rows first.  With a workspace, the last 40 % of
-// each XCD's list of an FA layer over one prompt is handed out at run time,
-// so XCDs that run faster than the others take over part of their tails.
+// head groups, heaviest causal rows first.  With a workspace, the last 20 % of
+// each XCD's list is handed out at run time, so XCDs that run faster than
+// the others take over part of their tails.
 #include "flux_device.h"
 #include "flux_internal.h"
 
@@ -633,25 +633,27 @@ __device__ __forceinline__ void decode_work(int bid, int G, int n_slots, int n_r
   g = w / n_req;
 }
 
-// Balanced order (p.wq: a caller's zeroed workspace; the host sets it only
-// for one prompt, one route decision per layer and items % 8 == 0).  The
-// eight XCDs finish equal static shares of an FA layer up to ~10 % apart,
-// and which XCD is slow changes from run to run, so only the first 60 % of
-// each XCD's list is static.  The rest of XCD x's list is queue x: a tail
-// workgroup of an FA layer takes the next item of the queue of the XCD it
-// runs on (hardware register XCC_ID), or, when that is empty, of the first
-// other queue with items left.  The grid has items / 8 more workgroups than
-// items; every tail workgroup either takes one item or finds all queues
-// empty and ends, and since there are at least as many tail workgroups as
-// tail items, every item is taken exactly once.  wq[0..7] count the items
-// taken from each queue, wq[8] the tail workgroups done; the last one sets
-// all nine back to zero, so the workspace is zero again when the launch
-// completes.  SA layers (short, equal items whose K/V sits in their own
-// XCD's L2) keep the fixed order: their tail workgroups take item blockIdx,
-// and the extra ones end.
+// Balanced order (p.wq: a caller's zeroed workspace; the host sets it for
+// layer-level routing when the items split into whole XCD shares and fill at
+// least one round of the GPU's workgroups).  The eight XCDs finish equal
+// static shares up to ~10 % apart, and which XCD is slow changes from run to
+// run, so only the first 80 % of each XCD's list is static.  The rest of XCD
+// x's list is queue x, counted by wq[x * kLine] (one counter per 128-byte
+// line).  The grid has items / 8 more workgroups than items.  A tail
+// workgroup whose blockIdx is below `items` first takes the next item of the
+// queue of the XCD it runs on (hardware register XCC_ID); when that is empty,
+// and for the extra workgroups, it reads all eight counters and tries only
+// the queues that still had items, in order from its own.  Every taken index
+// below the tail length is one item, so every item is taken at most once; a
+// workgroup ends only when every queue has handed out all its items, and
+// since there are at least as many tail workgroups as tail items, every item
+// is taken.  The counters are set back to zero by a one-workgroup kernel
+// launched after the attention kernel on the same stream, so the workspace
+// is zero again when the call completes and no workgroup waits for another.
 struct Balance {
-  static constexpr int kTailPct = 40;
-  int items, per, stat;  // items, items per XCD, static items per XCD
+  static constexpr int kTailPct = 20;
+  static constexpr int kLine = 32;  // int32 counters 128 bytes apart
+  int items, per, stat;             // items, items per XCD, static items per XCD
   __device__ __forceinline__ void init(int n_items) {
     items = n_items;
     per = n_items / 8;
@@ -664,19 +666,30 @@ struct Balance {
   __device__ __forceinline__ int take(const PrefillParams& p) const {
     const int x = __builtin_amdgcn_s_getreg((31 << 11) | 20) & 7;  // hwreg(HW_REG_XCC_ID)
     const int tail = per - stat;
+    if (static_cast<int>(blockIdx.x) < items) {
+      const int i = atomicAdd(&p.wq[x * kLine], 1);
+      if (i < tail) return (stat + i) * 8 + x;
+    }
+    int taken[8];
+#pragma unroll
+    for (int y = 0; y < 8; ++y)
+      taken[y] = __hip_atomic_load(&p.wq[y * kLine], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int k = 0; k < 8; ++k) {
       const int y = (x + k) & 7;
-      const int i = atomicAdd(&p.wq[y], 1);
+      int ty = taken[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) ty = y == j ? taken[j] : ty;  // taken[y] without a dynamic index
+      if (ty >= tail) continue;
+      const int i = atomicAdd(&p.wq[y * kLine], 1);
       if (i < tail) return (stat + i) * 8 + y;
     }
     return -1;
   }
-  __device__ __forceinline__ void done(const PrefillParams& p) const {  // thread 0 of a queue user
-    const int n_tail_wg = static_cast<int>(gridDim.x) - 8 * stat;
-    if (atomicAdd(&p.wq[8], 1) == n_tail_wg - 1)
-      for (int k = 0; k < 9; ++k) atomicExch(&p.wq[k], 0);
-  }
 };
+
+__global__ void balance_reset_kernel(int32_t* wq) {
+  if (threadIdx.x < 8) wq[threadIdx.x * Balance::kLine] = 0;
+}
 
 // SOFT: the soft-routed forward, O = r FA + (1 - r) SA with r per (request,
 // layer), with one softmax state (SoftOrder): the SA tiles come first; after
@@ -709,22 +722,12 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   Balance bal;
   bal.init(n_qt * p.hq * p.n_req);
   int bid = blockIdx.x;
-  bool queued = false;  // this workgroup took its item from the queues
   if (bal.tail_wg(p)) {
-    __shared__ int item_sh, queued_sh;
-    if (tid == 0) {
-      // the one prompt's route decides (the soft pass does FA's work)
-      const bool fa = SOFT || p.route[route_index(0, p.n_layers, p.layer, 1, 0)] != 0;
-      item_sh = fa ? bal.take(p) : (bid < bal.items ? bid : -1);
-      queued_sh = fa;
-    }
+    __shared__ int item_sh;
+    if (tid == 0) item_sh = bal.take(p);
     __syncthreads();
     bid = __builtin_amdgcn_readfirstlane(item_sh);
-    queued = __builtin_amdgcn_readfirstlane(queued_sh) != 0;
-    if (bid < 0) {
-      if (queued && tid == 0) bal.done(p);
-      return;
-    }
+    if (bid < 0) return;
   }
   decode_work(bid, p.wq != nullptr ? bal.items : static_cast<int>(gridDim.x), group, p.n_req, n_qt, p.hkv,
               p.route_heads > 1, hi, req, t, g);
@@ -748,10 +751,7 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   const int rb = __builtin_amdgcn_readlane(gv, 2), re = __builtin_amdgcn_readlane(gv, 3);
   const int rbyte = __builtin_amdgcn_readlane(gv, 4);
   const int q0 = t * BM;
-  if (q0 >= S) {
-    if (queued && tid == 0) bal.done(p);
-    return;
-  }
+  if (q0 >= S) return;
   const bool fa = SOFT || rbyte != 0;
   const int q_end = min(q0 + BM, S);
 
@@ -871,7 +871,6 @@ __global__ __launch_bounds__(BM * 2, OCC) void prefill_kernel(const PrefillParam
   } else {
     wa.store(p.out, tok0, p.hq, head, S, stage, lane);
   }
-  if (queued && tid == 0) bal.done(p);
 }
 
 template <int D, int BM>
@@ -885,7 +884,12 @@ hipError_t launch_typed(const PrefillParams& p, hipStream_t s) {
     prefill_kernel<D, BM, kBN, occ, true><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
   else
     prefill_kernel<D, BM, kBN, occ><<<dim3(static_cast<uint32_t>(grid)), dim3(BM * 2), 0, s>>>(p);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && p.wq != nullptr) {
+    balance_reset_kernel<<<1, 64, 0, s>>>(p.wq);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace

@@ -190,19 +190,22 @@ flux_status flux_build_block_mask_dynamic(const uint16_t* q, const uint16_t* k, 
  *             layers read the columns.
  * workspace   [device] NULL, or FLUX_PREFILL_WORKSPACE_BYTES (16-byte
  *             aligned, owned by the caller) that are all zero before the call;
- *             the call leaves them all zero again when it completes.  For an
- *             FA layer over one prompt, the last part of every XCD's share of
- *             the work is then handed out at run time, so XCDs that run
- *             faster than the others take over some of their work (other
- *             calls keep the fixed order).  Results are bitwise those without
- *             a workspace: only which workgroup computes a query block
- *             changes.  Calls that run at the same time need different
- *             workspaces.  A size below FLUX_PREFILL_WORKSPACE_BYTES or a
- *             misaligned pointer is FLUX_ERR_WORKSPACE.
+ *             the call leaves them all zero again when it completes (a
+ *             one-workgroup kernel that follows the attention kernel on the
+ *             stream clears them).  When the call has at least 768 query
+ *             blocks x heads in a multiple of 8, the last part of every XCD's
+ *             share of the work is then handed out at run time, so XCDs that
+ *             run faster than the others take over some of their work
+ *             (smaller calls keep the fixed order).  Results are bitwise
+ *             those without a workspace: only which workgroup computes a
+ *             query block changes.  Calls that run at the same time need
+ *             different workspaces.  A size below
+ *             FLUX_PREFILL_WORKSPACE_BYTES or a misaligned pointer is
+ *             FLUX_ERR_WORKSPACE.
  * Supported: head_dim in {64, 128}, block_size in {64, 128}, hq % hkv == 0,
  *            hq / hkv <= 16.  out may not alias q, k or v.
  */
-#define FLUX_PREFILL_WORKSPACE_BYTES ((size_t)64)
+#define FLUX_PREFILL_WORKSPACE_BYTES ((size_t)1024)
 
 /* FLUX_PREFILL_WORKSPACE_BYTES [host]. */
 size_t flux_attn_prefill_workspace_size(void);

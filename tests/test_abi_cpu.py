@@ -121,18 +121,19 @@ def prefill(**kw):
     (dict(sa=SA(64, 1, 0)), -1), (dict(sa=SA(64, -2, 1)), -1),
     (dict(mb=7), -1),                          # mask too small for max_seqlen
     (dict(d=96), -2), (dict(sa=SA(32, 1, 2)), -2), (dict(hq=34, hkv=2), -2),
-    (dict(ws=ctypes.c_void_p(0x4000), wsb=63), -3),                    # balancing workspace too small
-    (dict(ws=ctypes.c_void_p(0x4008), wsb=64), -3),                    # ... or not 16-byte aligned
-    (dict(ws=ctypes.c_void_p(0x4000), wsb=64, hq=5, hkv=2), -1),       # other checks still apply
+    (dict(ws=ctypes.c_void_p(0x4000), wsb=1023), -3),                  # balancing workspace too small
+    (dict(ws=ctypes.c_void_p(0x4000), wsb=64), -3),
+    (dict(ws=ctypes.c_void_p(0x4008), wsb=1024), -3),                  # ... or not 16-byte aligned
+    (dict(ws=ctypes.c_void_p(0x4000), wsb=1024, hq=5, hkv=2), -1),     # other checks still apply
 ])
 def test_prefill_validation(kw, code):
     assert prefill(**kw) == code
 
 
 def test_prefill_workspace_size():
-    """The balancing workspace is a fixed 64 bytes: 8 queue counters, one
-    count of finished workgroups, room to spare."""
-    assert lib.flux_attn_prefill_workspace_size() == _lib.FLUX_PREFILL_WORKSPACE_BYTES == 64
+    """The balancing workspace is a fixed 1024 bytes: 8 queue counters, each
+    on a 128-byte line of its own."""
+    assert lib.flux_attn_prefill_workspace_size() == _lib.FLUX_PREFILL_WORKSPACE_BYTES == 1024
 
 
 def test_decode_workspace_size():

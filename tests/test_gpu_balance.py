@@ -1,17 +1,17 @@
-"""GPU prefill with the balancing workspace.  For an FA layer (or the soft
-pass) over one prompt the tail of every XCD's work list is handed out at run
-time, so the workgroup that computes a query block changes, but nothing else
-does: outputs must equal the fixed-order launch bit for bit (the same tiles
-in the same order per query block), every query block must be computed, and
-the workspace must be zero again after every call, so that one workspace
-serves calls of different shapes in a row.  Cases: a 32K prompt (FA through
-the queues, SA in the fixed order with the extra workgroups ending at once),
-a prompt shorter than max_seqlen (queue items past its end), the soft pass,
-64-wide heads and 64-row blocks, shapes below one round of workgroups and a
-packed batch (fixed order with a workspace passed), and the binding's
+"""GPU prefill with the balancing workspace.  The tail of every XCD's work
+list is handed out at run time, so the workgroup that computes a query block
+changes, but nothing else does: outputs must equal the fixed-order launch bit
+for bit (the same tiles in the same order per query block), every query
+block must be computed, and the workspace must be zero again after every call
+(the launch that follows the kernel clears it), so that one workspace serves
+calls of different shapes in a row.  Cases: a 32K prompt (FA and SA layers
+through the queues), a prompt shorter than max_seqlen (queue items past its
+end), the soft pass, 64-wide heads and 64-row blocks, packed batches with
+mixed routes, shapes below one round of workgroups or with a work count that
+is not a multiple of 8 (fixed order with a workspace passed), the binding's
 per-stream workspace, and a balanced launch replayed from a HIP graph.  The
-oracle comparisons of every other prefill test run
-with the workspace too (the binding's default)."""
+oracle comparisons of every other prefill test run with the workspace too
+(the binding's default)."""
 
 import pytest
 import torch
@@ -79,7 +79,7 @@ def test_single_prompt_32k_fa_and_sa():
 
 
 def test_prompt_shorter_than_max_seqlen():
-    """Queue items past the prompt's end end at once and still count as done."""
+    """Queue items past the prompt's end are taken and end at once."""
     S, max_len, hq, hkv, d = 5000, 8192, 32, 8, 128
     say("balanced prefill, prompt of 5000 under max_seqlen 8192")
     q, k, v, cu, sa, rp, ci = inputs([S], hq, hkv, d, 128, 8, 8202)
@@ -112,12 +112,13 @@ def test_soft_pass():
 
 @pytest.mark.parametrize("shape", [
     # (lens, hq, hkv, d, B): balanced with 64-wide heads and 64-row blocks;
-    # below one round of workgroups (fixed order even with a workspace); a
-    # packed batch (fixed order)
+    # below one round of workgroups, or 131 blocks x 20 heads (not a multiple
+    # of 8): the fixed order even with a workspace; a packed batch (balanced)
     ([4096], 16, 4, 64, 64),
     ([4000], 16, 4, 128, 64),
     ([512], 4, 2, 64, 64),
     ([300], 4, 2, 128, 128),
+    ([16700], 20, 4, 128, 128),
     ([130, 7000], 8, 8, 64, 64),
 ])
 def test_other_shapes(shape):
@@ -129,6 +130,19 @@ def test_other_shapes(shape):
     ws = new_workspace()
     for layer in (0, 1):
         check_pair(q, k, v, cu, S, route, layer, rp, ci, sa, ws, f"{shape} layer {layer}")
+
+
+def test_packed_batch_with_mixed_routes():
+    """Four prompts, FA for two and SA for the other two in one launch, every
+    item through the same queues; then all four under each route."""
+    lens = [3000, 9000, 20000, 512]
+    S, hq, hkv, d = max(lens), 32, 8, 128
+    say("balanced prefill, packed batch with mixed routes")
+    q, k, v, cu, sa, rp, ci = inputs(lens, hq, hkv, d, 128, 8, 8707)
+    route = torch.tensor([[1, 1, 0], [0, 1, 0], [1, 1, 0], [0, 1, 0]], dtype=torch.uint8, device=DEV)
+    ws = new_workspace()
+    for layer in (0, 1, 2):
+        check_pair(q, k, v, cu, S, route, layer, rp, ci, sa, ws, f"packed layer {layer}")
 
 
 def test_stream_workspace_is_reused_and_stays_zero():
