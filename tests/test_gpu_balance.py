@@ -7,7 +7,7 @@ block must be computed, and the workspace must be zero again after every call
 calls of different shapes in a row.  Cases: a 32K prompt (FA and SA layers
 through the queues), a prompt shorter than max_seqlen (queue items past its
 end), the soft pass, 64-wide heads and 64-row blocks, packed batches with
-mixed routes, shapes below one round of workgroups or with a work count that
+mixed routes and with empty and one-token requests, shapes below one round of workgroups or with a work count that
 is not a multiple of 8 (fixed order with a workspace passed), the binding's
 per-stream workspace, and a balanced launch replayed from a HIP graph.  The
 oracle comparisons of every other prefill test run with the workspace too
@@ -143,6 +143,35 @@ def test_packed_batch_with_mixed_routes():
     ws = new_workspace()
     for layer in (0, 1, 2):
         check_pair(q, k, v, cu, S, route, layer, rp, ci, sa, ws, f"packed layer {layer}")
+
+
+def test_packed_batch_with_empty_and_one_token_requests():
+    """Through the queues, a packed batch whose requests include two empty
+    ones and a one-token one (its row is V's first row); every other request
+    is checked against the oracle on rows across it, under both routes."""
+    lens = [3000, 0, 9000, 1, 0, 12000]
+    S, hq, hkv, d, B = max(lens), 32, 8, 128, 128
+    say("balanced prefill, packed batch with empty and one-token requests")
+    q, k, v, cu, sa, rp, ci = inputs(lens, hq, hkv, d, B, 8, 8808)
+    route = torch.tensor([[1, 0], [0, 1], [0, 1], [1, 0], [1, 0], [0, 1]], dtype=torch.uint8, device=DEV)
+    ws = new_workspace()
+    m = oracle.block_mask(oracle.num_blocks(S, B), 1, 8)
+    qh, kh, vh = (t.float().cpu().numpy() for t in (q, k, v))
+    cu_h = [0]
+    for n in lens:
+        cu_h.append(cu_h[-1] + n)
+    for layer in (0, 1):
+        out = check_pair(q, k, v, cu, S, route, layer, rp, ci, sa, ws, f"empty/one-token layer {layer}")
+        got = out.float().cpu().numpy()
+        for r, n in enumerate(lens):
+            if n == 0:
+                continue
+            a = cu_h[r]
+            rows = sorted(set(range(0, n, max(1, n // 9))) | {n - 1})
+            heads = [0, 13, 31]
+            ref = oracle.attention_prefill(qh[a:a + n], kh[a:a + n], vh[a:a + n], bool(route[r, layer]), m, B,
+                                           rows=rows, heads=heads)
+            assert_attn_close(got[a:a + n][rows][:, heads], ref, f"request {r} layer {layer}")
 
 
 def test_stream_workspace_is_reused_and_stays_zero():
