@@ -21,7 +21,7 @@ struct PrefillParams {
   int32_t route_heads;  // route decisions per (request, layer): 1, or hkv (one per kv head)
   const float* rsoft;   // non-null: soft-routed forward, weight of FA per (request, layer)
   float scale;
-  int32_t* wq;          // non-null: balanced order, the caller's zeroed workspace (9 counters)
+  int32_t* wq;          // non-null: balanced order, the caller's zeroed workspace (8 queue counters)
 };
 
 struct DecodeParams {
