@@ -192,11 +192,11 @@ flux_status flux_build_block_mask_dynamic(const uint16_t* q, const uint16_t* k, 
  *             aligned, owned by the caller) that are all zero before the call;
  *             the call leaves them all zero again when it completes (a
  *             one-workgroup kernel that follows the attention kernel on the
- *             stream clears them).  When the call has at least 768 query
- *             blocks x heads in a multiple of 8, the last part of every XCD's
- *             share of the work is then handed out at run time, so XCDs that
- *             run faster than the others take over some of their work
- *             (smaller calls keep the fixed order).  Results are bitwise
+ *             stream clears them).  When ceil(max_seqlen / block_size) x hq
+ *             x n_req is at least 768 and a multiple of 8, the last part of
+ *             every XCD's share of the work is then handed out at run time,
+ *             so XCDs that run faster than the others take over some of their
+ *             work (other calls keep the fixed order).  Results are bitwise
  *             those without a workspace: only which workgroup computes a
  *             query block changes.  Calls that run at the same time need
  *             different workspaces.  A size below
